@@ -1,0 +1,107 @@
+"""Plain causal softmax attention in fp64 - the quantity the method approximates.
+
+TEST INFRASTRUCTURE ONLY (see ``oracle/__init__.py``).
+
+The operation is forward prefill attention with equal query and key lengths and
+a causal mask ([KG-en] §"Application Boundaries and Engineering Decisions";
+[MTP] §TL;DR and its comparison table, row "Scope"): for every batch b, query
+head h and query position i,
+
+    O[b,i,h,:] = sum_{j<=i} w_ij V[b,j,g,:],
+    w_ij = exp(sm * <Q[b,i,h,:], K[b,j,g,:]> - m_i) / sum_{j'<=i} exp(sm * <Q_i, K_j'> - m_i),
+
+with m_i the row maximum (it cancels; it only keeps exp in range), sm the
+softmax scale (1/sqrt(d_qk) unless given) and g the key/value head of query head
+h.  The pages measure accuracy as RMS error against fp64 for a single attention
+call ([KG-en] §"Performance Benchmarks"; [MTP] §"How accurate is ZYFA's FP8
+attention?"), so this is evaluated in fp64.
+
+Readings (the pages are silent): grouped-query attention maps query head h to
+key/value head floor(h / (Hq / Hkv)) (consecutive groups, the flash_attn
+convention behind the "drop-in flash_attn_func interface", [MTP] §TL;DR);
+tensors are (B, S, H, d), contiguous in d.
+
+Every query row is computed independently from the definition; rows are only
+grouped into chunks to bound memory.
+"""
+import numpy as np
+
+from .e4m3 import decode_e4m3
+
+
+def dequantize(codes, scale):
+    """x_hat = scale * decode(code), as float64."""
+    return float(scale) * decode_e4m3(codes)
+
+
+def kv_head(h, Hq, Hkv):
+    """Key/value head used by query head h (consecutive groups)."""
+    return h // (Hq // Hkv)
+
+
+def _rows_of(rows, S):
+    if rows is None:
+        return np.arange(S)
+    return np.asarray(rows, dtype=np.int64)
+
+
+def attention_fp64(q, k, v, sm_scale=None, causal=True, rows=None, chunk=512):
+    """Causal (or full) softmax attention in fp64.
+
+    q: (B, S, Hq, d_qk), k: (B, S, Hkv, d_qk), v: (B, S, Hkv, d_v), any real dtype.
+    rows: optional 1-D array of query positions to evaluate (default: all).
+    Returns O of shape (B, len(rows), Hq, d_v), float64.
+    """
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    B, S, Hq, dqk = q.shape
+    Hkv = k.shape[2]
+    dv = v.shape[3]
+    assert k.shape == (B, S, Hkv, dqk) and v.shape == (B, S, Hkv, dv)
+    assert Hq % Hkv == 0
+    sm = 1.0 / np.sqrt(dqk) if sm_scale is None else float(sm_scale)
+    rows = _rows_of(rows, S)
+    out = np.empty((B, len(rows), Hq, dv), dtype=np.float64)
+    keys = np.arange(S)
+    for b in range(B):
+        for h in range(Hq):
+            g = kv_head(h, Hq, Hkv)
+            kk = k[b, :, g, :]
+            vv = v[b, :, g, :]
+            for c0 in range(0, len(rows), chunk):
+                r = rows[c0:c0 + chunk]
+                n = (int(r.max()) + 1) if causal else S  # keys any row here can see
+                logits = sm * (q[b, r, h, :] @ kk[:n].T)
+                if causal:
+                    logits = np.where(keys[None, :n] <= r[:, None], logits, -np.inf)
+                m = logits.max(axis=1, keepdims=True)
+                w = np.exp(logits - m)
+                w /= w.sum(axis=1, keepdims=True)
+                out[b, c0:c0 + len(r), h, :] = w @ vv[:n]
+    return out
+
+
+def attention_weights_fp64(q, k, sm_scale=None, causal=True):
+    """The full weight matrix w[b, h, i, j] (small shapes only)."""
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    B, S, Hq, dqk = q.shape
+    Hkv = k.shape[2]
+    sm = 1.0 / np.sqrt(dqk) if sm_scale is None else float(sm_scale)
+    w = np.empty((B, Hq, S, S))
+    mask = np.tril(np.ones((S, S), dtype=bool)) if causal else np.ones((S, S), dtype=bool)
+    for b in range(B):
+        for h in range(Hq):
+            g = kv_head(h, Hq, Hkv)
+            logits = np.where(mask, sm * (q[b, :, h, :] @ k[b, :, g, :].T), -np.inf)
+            e = np.exp(logits - logits.max(axis=1, keepdims=True))
+            w[b, h] = e / e.sum(axis=1, keepdims=True)
+    return w
+
+
+def rel_rms(x, ref):
+    """Relative RMS error ||x - ref||_2 / ||ref||_2 over all elements."""
+    x = np.asarray(x, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    return float(np.sqrt(np.sum((x - ref) ** 2)) / np.sqrt(np.sum(ref ** 2)))

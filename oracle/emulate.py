@@ -1,0 +1,169 @@
+"""Step-by-step CPU emulation of the FP8 method (block-scaled, rounded-sum softmax).
+
+TEST INFRASTRUCTURE ONLY (see ``oracle/__init__.py``).
+
+The method approximates ``attention64.attention_fp64``: the probabilities P are
+rounded to FP8 e4m3 before the P.V product.  This module takes the pages' steps
+in their order, in fp64 except where the method itself rounds:
+
+1. Scores.  s_ij = sum_c decode(Q8[i,c]) * decode(K8[j,c]) - the product of the
+   FP8 codes' values that the FP8 matrix instruction forms (exact in fp64: each
+   product has at most 8 significant bits and the sum spans < 53 bits).
+   t_ij = s_ij * q_scale * k_scale * sm * log2(e) is the score in log2 units.
+2. Causal mask: keys j > i are excluded ([KG-en] §"Application Boundaries").
+3. Per-64-key-block power-of-2 scale.  Each 64-key block of probabilities is
+   scaled by a power of two before rounding, and the scaled matrix instruction
+   takes the factor back out ([MTP] §"Per-block scaling and a rounded row sum";
+   [KG-en] §"ZYFA's Technical Solutions").  Reading: the power is chosen per
+   (query row, 64-key block) from M_ib = ceil(max_{j in block b, j<=i} t_ij),
+   so that the block's largest probability lands in (128, 256] - the top binade
+   of e4m3 below its 448 maximum - and the probability is taken relative to
+   the block's own integer maximum (independent of block order).
+4. Probabilities, one of two paths:
+   * exact: p~_ij = e4m3_RNE(2^(t_ij - M_ib + 8)) - a true exponential, rounded;
+   * Lean P: the e4m3 code of 2^x is about 8x + const because the code grows
+     by 8 per doubling ([MTP] §"Lean P: one multiply-add instead of an
+     exponential"; [KG-en] §"ZYFA's Technical Solutions").  With
+     x = t_ij - M_ib + 8 and code(2^n) = 8n + 56 the code is the single
+     multiply-add A*s_ij + B_ib, A = 8*q_scale*k_scale*sm*log2(e),
+     B_ib = 120 - 8*M_ib, followed by one conversion to an integer.  Reading:
+     the conversion rounds to nearest, ties to even, and saturates to [0, 126]
+     (codes below 0 are probability 0; 126 = 448 is never reached since the
+     block maximum maps to code <= 120).  p~_ij = decode(code).
+5. Rounded row sum: l_ib = sum_j p~_ij, the sum of the rounded probabilities,
+   not of the unrounded ones ([MTP] ibid.; [KG-zh] §技术解法 gives the reason:
+   values that round to zero would otherwise still count in the denominator).
+6. Combination over blocks (the online-softmax recurrence written in closed
+   form; it is exact because every block factor is a power of two):
+       O_i = v_scale * sum_b 2^(M_ib - R_i) sum_j p~_ij decode(V8_j)
+                     / sum_b 2^(M_ib - R_i) l_ib,        R_i = max_b M_ib.
+   The common 2^-8 of step 3 and the choice of R_i cancel between numerator and
+   denominator; R_i only keeps 2^(.) in range.
+
+``rounding=False`` (exact path only) skips the e4m3 rounding in step 4; the
+result is then the plain definition, which pins this module to
+``attention64`` (tests/test_oracle_emulate.py).
+"""
+import numpy as np
+
+from .e4m3 import decode_e4m3, encode_e4m3_rne, round_to_e4m3
+from .attention64 import kv_head, _rows_of
+
+LOG2E = 1.4426950408889634
+BLOCK_KEYS = 64
+
+
+def _block_probs(t, valid, p_mode, rounding, s=None, A=None):
+    """Steps 3-5 for one chunk of rows.
+
+    t, valid: (R, nb, 64) log2-domain scores and the causal/tail validity mask.
+    Returns (p~ (R, nb, 64) float64, M (R, nb) float64, block_has_keys (R, nb)).
+    """
+    tm = np.where(valid, t, -np.inf)
+    has = valid.any(axis=2)
+    bmax = tm.max(axis=2)
+    M = np.where(has, np.ceil(np.where(has, bmax, 0.0)), 0.0)
+    if p_mode == "exact":
+        x = t - M[:, :, None] + 8.0
+        p = np.exp2(np.where(valid, x, -np.inf))
+        if rounding:
+            p = round_to_e4m3(p)
+    elif p_mode == "lean":
+        if not rounding:
+            raise ValueError("Lean P always produces integer codes")
+        B = 120.0 - 8.0 * M
+        code = np.rint(A * s + B[:, :, None])
+        code = np.clip(code, 0, 126)
+        code = np.where(valid, code, 0).astype(np.uint8)
+        p = decode_e4m3(code)
+    else:
+        raise ValueError(p_mode)
+    p = np.where(valid, p, 0.0)
+    return p, M, has
+
+
+def emulate_fp8(q8, k8, v8, q_scale, k_scale, v_scale, sm_scale=None, p_mode="exact",
+                causal=True, rows=None, rounding=True, chunk=256, return_lse=False):
+    """Emulate the FP8 method on e4m3 codes (uint8 arrays, (B, S, H, d) layout).
+
+    Returns O (B, len(rows), Hq, d_v) float64.  With ``return_lse`` also returns
+    the per-row natural-log normaliser of the *rounded* weights,
+    ln(sum_b 2^(M_ib-8) l_ib) / ... expressed as log2: log2L (B, len(rows), Hq).
+    """
+    q8 = np.asarray(q8, dtype=np.uint8)
+    k8 = np.asarray(k8, dtype=np.uint8)
+    v8 = np.asarray(v8, dtype=np.uint8)
+    B, S, Hq, dqk = q8.shape
+    Hkv = k8.shape[2]
+    dv = v8.shape[3]
+    sm = 1.0 / np.sqrt(dqk) if sm_scale is None else float(sm_scale)
+    C = float(q_scale) * float(k_scale) * sm * LOG2E
+    A = np.float64(np.float32(8.0 * C))
+    rows = _rows_of(rows, S)
+    out = np.empty((B, len(rows), Hq, dv))
+    log2L = np.empty((B, len(rows), Hq))
+    qd = decode_e4m3(q8)
+    kd = decode_e4m3(k8)
+    vd = decode_e4m3(v8)
+    for b in range(B):
+        for h in range(Hq):
+            g = kv_head(h, Hq, Hkv)
+            for c0 in range(0, len(rows), chunk):
+                r = rows[c0:c0 + chunk]
+                n = (int(r.max()) + 1) if causal else S
+                nb = (n + BLOCK_KEYS - 1) // BLOCK_KEYS
+                npad = nb * BLOCK_KEYS
+                s = np.zeros((len(r), npad))
+                s[:, :n] = qd[b, r, h, :] @ kd[b, :n, g, :].T
+                keys = np.arange(npad)
+                valid = np.broadcast_to(keys[None, :] < n, (len(r), npad))
+                if causal:
+                    valid = valid & (keys[None, :] <= r[:, None])
+                s3 = s.reshape(len(r), nb, BLOCK_KEYS)
+                v3 = valid.reshape(len(r), nb, BLOCK_KEYS)
+                p, M, has = _block_probs(s3 * C, v3, p_mode, rounding, s=s3, A=A)
+                Rref = np.max(np.where(has, M, -np.inf), axis=1)
+                fac = np.where(has, np.exp2(M - Rref[:, None]), 0.0)
+                l = p.sum(axis=2)
+                den = (fac * l).sum(axis=1)
+                W = (p * fac[:, :, None]).reshape(len(r), npad)[:, :n]
+                num = W @ vd[b, :n, g, :]
+                out[b, c0:c0 + len(r), h, :] = float(v_scale) * (num / den[:, None])
+                log2L[b, c0:c0 + len(r), h] = np.log2(den) + Rref - 8.0
+    if return_lse:
+        return out, log2L
+    return out
+
+
+def block_probabilities(q8, k8, q_scale, k_scale, sm_scale=None, p_mode="exact", i=0, b=0, h=0,
+                        Hkv=None):
+    """The rounded probabilities p~ (nb, 64) and exponents M (nb,) of one query row.
+
+    For tests of the per-block structure on small inputs.
+    """
+    q8 = np.asarray(q8, dtype=np.uint8)
+    k8 = np.asarray(k8, dtype=np.uint8)
+    B, S, Hq, dqk = q8.shape
+    Hkv = k8.shape[2] if Hkv is None else Hkv
+    sm = 1.0 / np.sqrt(dqk) if sm_scale is None else float(sm_scale)
+    C = float(q_scale) * float(k_scale) * sm * LOG2E
+    A = np.float64(np.float32(8.0 * C))
+    g = kv_head(h, Hq, Hkv)
+    n = i + 1
+    nb = (n + BLOCK_KEYS - 1) // BLOCK_KEYS
+    s = np.zeros((1, nb * BLOCK_KEYS))
+    s[:, :n] = decode_e4m3(q8[b, i:i + 1, h, :]) @ decode_e4m3(k8[b, :n, g, :]).T
+    valid = (np.arange(nb * BLOCK_KEYS) < n)[None, :]
+    s3 = s.reshape(1, nb, BLOCK_KEYS)
+    p, M, has = _block_probs(s3 * C, valid.reshape(1, nb, BLOCK_KEYS), p_mode, True, s=s3, A=A)
+    return p[0], M[0]
+
+
+def encode_probability_lean(y):
+    """Lean-P code for a log2-domain value y = t - M + 8 (y <= 8): rint(8y + 56) in [0, 126]."""
+    return np.clip(np.rint(8.0 * np.asarray(y, dtype=np.float64) + 56.0), 0, 126).astype(np.uint8)
+
+
+def encode_probability_exact(y):
+    """Exact-path code for y: e4m3_RNE(2^y)."""
+    return encode_e4m3_rne(np.exp2(np.asarray(y, dtype=np.float64)))
