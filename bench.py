@@ -1,0 +1,230 @@
+"""Benchmark: causal FP8 prefill attention throughput on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload gauss32k]
+                    [--mode lean|exact] [--dtype fp8|bf16] [--no-cpu-baseline]
+
+One step = one attn_fwd_fp8 call over the whole workload (Q,K,V resident in HBM
+when timing starts).  Throughput uses the causal FLOP count
+2*B*Hq*S^2*(d_qk+d_v)/2.  Prints one JSON line.
+"""
+import argparse
+import json
+import os
+import subprocess
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "causal prefill attention TFLOP/s & % FP8 peak (d=128, S=32K); RMS err vs fp64"
+# MI355X published dense peaks, TFLOP/s
+PEAK_TFLOPS = {"fp8": 5000.0, "bf16": 2500.0}
+# The pages' own figure for this workload (ZYFA, FP8, d=128, 32K tokens, Gaussian inputs, MI355X)
+PAGES_TFLOPS = {("gauss32k", "fp8"): 2672.0}
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="gauss32k")
+    ap.add_argument("--mode", default="lean", choices=["lean", "exact"])
+    ap.add_argument("--dtype", default="fp8", choices=["fp8", "bf16"])
+    ap.add_argument("--both-modes", action="store_true", default=True,
+                    help="also time the other FP8 probability path (reported under 'paths')")
+    ap.add_argument("--no-both-modes", dest="both_modes", action="store_false")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    return ap.parse_args()
+
+
+def sclk_mhz():
+    """Current shader clock from amd-smi (None if unavailable)."""
+    try:
+        r = subprocess.run(["amd-smi", "metric", "-g", "0", "--clock", "--json"], capture_output=True,
+                           text=True, timeout=20)
+        data = json.loads(r.stdout)
+        if isinstance(data, list):
+            data = data[0]
+        clk = data.get("clock", data)
+        gfx = clk.get("gfx_0") or clk.get("GFX_0") or {}
+        v = gfx.get("clk")
+        if isinstance(v, dict):
+            v = v.get("value")
+        return float(v) if v is not None else None
+    except Exception:
+        return None
+
+
+def time_launches(fn, steps, warmup, stream):
+    import torch
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    t0 = time.perf_counter()
+    for i in range(steps):
+        starts[i].record(stream)
+        fn()
+        ends[i].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    per = sorted(s.elapsed_time(e) for s, e in zip(starts, ends))   # ms, HIP events on the launch stream
+    return wall, per
+
+
+def cpu_baseline(w, d, out_gpu, seconds, dtype):
+    """Time the CPU oracle (fp64 attention) on a bounded sample of the same workload and
+    compare the GPU output on those rows.  Returns the cpu_baseline object."""
+    import numpy as np
+    from threadpoolctl import threadpool_info
+    from oracle.attention64 import attention_fp64, dequantize, rel_rms
+
+    threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+    S = w.S
+    rows_per_chunk = 64
+    # rows spread over the sequence, longest prefixes first
+    order = np.linspace(S - 1, 0, 512).astype(np.int64)
+    heads = [0, w.Hq // 2, w.Hq - 1]
+    flops = 0.0
+    done_rows = []
+    errs_num, errs_den = 0.0, 0.0
+    t0 = time.perf_counter()
+    i = 0
+    while time.perf_counter() - t0 < seconds and i < len(order):
+        rows = np.sort(order[i:i + rows_per_chunk])
+        i += rows_per_chunk
+        for h in heads:
+            g = h // (w.Hq // w.Hkv)
+            if dtype == "fp8":
+                q = dequantize(d["q8"][:, :, h:h + 1].numpy(), d["q_scale"])
+                k = dequantize(d["k8"][:, :, g:g + 1].numpy(), d["k_scale"])
+                v = dequantize(d["v8"][:, :, g:g + 1].numpy(), d["v_scale"])
+            else:
+                q = d["q"][:, :, h:h + 1].float().numpy()
+                k = d["k"][:, :, g:g + 1].float().numpy()
+                v = d["v"][:, :, g:g + 1].float().numpy()
+            ts = time.perf_counter()
+            ref = attention_fp64(q, k, v, rows=rows)
+            flops += float(np.sum(2.0 * (rows + 1) * (w.d_qk + w.d_v)))
+            got = out_gpu[:, rows, h:h + 1].astype(np.float64)
+            errs_num += float(np.sum((got - ref) ** 2))
+            errs_den += float(np.sum(ref ** 2))
+            done_rows.append(len(rows))
+    el = time.perf_counter() - t0
+    return {
+        "value": flops / el / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+        "sample": f"fp64 attention (oracle/attention64.py, numpy+BLAS) on {sum(done_rows)//len(heads)} query rows "
+                  f"(spread over 0..S-1, longest first) x heads {heads} of the {w.name} workload, "
+                  f"{el:.1f} s; FLOPs counted 2*(i+1)*(d_qk+d_v) per row",
+        "gpu_rel_rms_vs_oracle_on_sample": float(np.sqrt(errs_num / errs_den)),
+        "cpu_model": _cpu_model(),
+        "os_cpu_count": os.cpu_count(),
+    }
+
+
+def _cpu_model():
+    try:
+        for ln in open("/proc/cpuinfo"):
+            if ln.startswith("model name"):
+                return ln.split(":", 1)[1].strip()
+    except Exception:
+        pass
+    return None
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); heads are "
+              f"independent, so a multi-GPU run is one independent launch per GPU on its share of heads.",
+              file=sys.stderr)
+        sys.exit(2)
+    import numpy as np
+    import torch
+    from fp8_causal_prefill_tiled_amd import binding
+    from fp8_causal_prefill_tiled_amd import workloads as W
+
+    w = W.WORKLOADS[args.workload]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream(dev)
+    flops = w.causal_flops
+    peak = PEAK_TFLOPS[args.dtype]
+
+    if args.dtype == "fp8":
+        d = W.make_fp8(w)
+        q, k, v = (d[n].to(dev) for n in ("q8", "k8", "v8"))
+        out = torch.empty((w.B, w.S, w.Hq, w.d_v), dtype=torch.bfloat16, device=dev)
+
+        def make_fn(mode):
+            return lambda: binding.attn_fwd_fp8(q, k, v, d["q_scale"], d["k_scale"], d["v_scale"],
+                                                p_mode=mode, out=out, stream=stream)
+        modes = [args.mode] + ([m for m in ("lean", "exact") if m != args.mode] if args.both_modes else [])
+    else:
+        d = W.make_bf16(w)
+        q, k, v = (d[n].to(dev) for n in ("q", "k", "v"))
+        out = torch.empty((w.B, w.S, w.Hq, w.d_v), dtype=torch.bfloat16, device=dev)
+
+        def make_fn(mode):
+            return lambda: binding.attn_fwd_bf16(q, k, v, out=out, stream=stream)
+        modes = ["exact"]
+    torch.cuda.synchronize()
+
+    paths = {}
+    clk_before = sclk_mhz()
+    for mode in reversed(modes):          # headline mode last: its output stays in `out`
+        wall, per = time_launches(make_fn(mode), args.steps, args.warmup, stream)
+        avg_ms = sum(per) / len(per)
+        paths[mode] = {
+            "tflops": flops * args.steps / wall / 1e12,
+            "ms_per_step": wall / args.steps * 1e3,
+            "kernel_ms_avg": avg_ms, "kernel_ms_median": per[len(per) // 2],
+            "kernel_ms_min": per[0], "kernel_ms_max": per[-1],
+            "frac_of_peak": flops / (avg_ms * 1e-3) / 1e12 / peak,
+        }
+    clk_after = sclk_mhz()
+    head = paths[modes[0]]
+    value = head["tflops"]
+    achieved = flops / (head["kernel_ms_avg"] * 1e-3) / 1e12
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        out_np = out.float().cpu().numpy()
+        cpu = cpu_baseline(w, d, out_np, args.cpu_seconds, args.dtype)
+
+    pages = PAGES_TFLOPS.get((w.name, args.dtype))
+    res = {
+        "metric": METRIC,
+        "value": value,
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": head["ms_per_step"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": (value / pages) if pages else None,
+        "dtype": args.dtype,
+        "data": "synthetic (seeded N(0,1), per-tensor e4m3 quantisation)" if args.dtype == "fp8"
+                else "synthetic (seeded N(0,1) rounded to bf16)",
+        "config": {"workload": w.name, "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv, "S": w.S, "d_qk": w.d_qk,
+                   "d_v": w.d_v, "causal": True, "p_mode": modes[0] if args.dtype == "fp8" else None,
+                   "causal_tflop_per_step": flops / 1e12},
+        "frac_of_peak": value / peak,
+        "roofline": {"bound": "mfma", "achieved": achieved, "peak": peak, "unit": "TFLOP/s",
+                     "frac": achieved / peak, "traffic": None,
+                     "kernel": f"{args.dtype}_causal_fwd", "per_launch_tflop": flops / 1e12},
+        "paths": paths,
+        "sclk_mhz": {"before": clk_before, "after": clk_after},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(res))
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,156 @@
+"""ctypes binding of libattnfwd.so (argument marshalling only).
+
+Every step of the attention runs in the library's HIP kernels; this module only
+turns torch tensors into (pointer, shape) arguments, passes torch's current HIP
+stream, and raises ``AttnError`` on a non-OK status.  It fails loudly when the
+library has not been built - there is no fallback implementation.
+"""
+import ctypes
+import math
+import os
+import subprocess
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_PKG, "libattnfwd.so")
+
+ATTN_OK, ATTN_E_INVALID_ARG, ATTN_E_UNSUPPORTED, ATTN_E_HIP = 0, 1, 2, 3
+P_EXACT, P_LEAN = 0, 1
+_P_MODES = {"exact": P_EXACT, "lean": P_LEAN, P_EXACT: P_EXACT, P_LEAN: P_LEAN}
+
+_EXPORTS = ("attn_fwd_fp8", "attn_fwd_bf16", "attn_last_error", "attn_abi_version")
+
+
+class AttnError(RuntimeError):
+    def __init__(self, status, message):
+        super().__init__(f"status {status}: {message}")
+        self.status = status
+
+
+_lib = None
+
+
+def library_path():
+    return _LIB_PATH
+
+
+def load_library():
+    """Load libattnfwd.so once; raise if it is missing."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH):
+        raise ImportError(f"{_LIB_PATH} is not built; run `python -m fp8_causal_prefill_tiled_amd.build`")
+    lib = ctypes.CDLL(_LIB_PATH)
+    vp, f, i = ctypes.c_void_p, ctypes.c_float, ctypes.c_int
+    lib.attn_fwd_fp8.argtypes = [vp, vp, vp, vp, f, f, f, f, i, i, i, i, i, i, i, i, vp]
+    lib.attn_fwd_fp8.restype = i
+    lib.attn_fwd_bf16.argtypes = [vp, vp, vp, vp, f, i, i, i, i, i, i, i, vp]
+    lib.attn_fwd_bf16.restype = i
+    lib.attn_last_error.argtypes = []
+    lib.attn_last_error.restype = ctypes.c_char_p
+    lib.attn_abi_version.argtypes = []
+    lib.attn_abi_version.restype = i
+    _lib = lib
+    return lib
+
+
+def attn_last_error():
+    return load_library().attn_last_error().decode()
+
+
+def exported_symbols():
+    """Dynamic symbols exported by the built library (via `nm -D`)."""
+    out = subprocess.run(["nm", "-D", "--defined-only", _LIB_PATH], capture_output=True, text=True, check=True)
+    return {ln.split()[-1] for ln in out.stdout.splitlines() if ln.strip()}
+
+
+def _check(status):
+    if status != ATTN_OK:
+        raise AttnError(status, attn_last_error())
+
+
+def _stream_ptr(stream, device):
+    if stream is None:
+        stream = torch.cuda.current_stream(device)
+    return stream.cuda_stream
+
+
+def _bshd(x, name):
+    if x.dim() != 4:
+        raise ValueError(f"{name} must be (B, S, H, d), got shape {tuple(x.shape)}")
+    if not x.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if not x.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    return x.shape
+
+
+def attn_fwd_fp8_raw(q, k, v, o, q_scale, k_scale, v_scale, softmax_scale, B, Hq, Hkv, S, d_qk, d_v,
+                     causal, p_mode, stream=0):
+    """Direct C call with integer pointers; returns the status code (no exception)."""
+    return load_library().attn_fwd_fp8(q, k, v, o, q_scale, k_scale, v_scale, softmax_scale,
+                                       B, Hq, Hkv, S, d_qk, d_v, causal, p_mode, stream)
+
+
+def attn_fwd_bf16_raw(q, k, v, o, softmax_scale, B, Hq, Hkv, S, d_qk, d_v, causal, stream=0):
+    return load_library().attn_fwd_bf16(q, k, v, o, softmax_scale, B, Hq, Hkv, S, d_qk, d_v, causal, stream)
+
+
+def attn_fwd_fp8(q8, k8, v8, q_scale, k_scale, v_scale, softmax_scale=None, causal=True,
+                 p_mode="exact", out=None, stream=None):
+    """Causal FP8 attention; q8/k8/v8 are e4m3fn bytes (uint8 or float8_e4m3fn), (B,S,H,d).
+
+    Returns the bf16 output (B, S, Hq, d_v), enqueued on ``stream`` (default:
+    torch's current stream of the inputs' device).
+    """
+    for t, n in ((q8, "q8"), (k8, "k8"), (v8, "v8")):
+        if t.dtype not in (torch.uint8, torch.float8_e4m3fn):
+            raise TypeError(f"{n} must hold e4m3fn bytes (uint8 or float8_e4m3fn), got {t.dtype}")
+    B, S, Hq, dqk = _bshd(q8, "q8")
+    Bk, Sk, Hkv, dk = _bshd(k8, "k8")
+    Bv, Sv, Hv, dv = _bshd(v8, "v8")
+    if (Bk, Sk, dk) != (B, S, dqk) or (Bv, Sv, Hv) != (B, S, Hkv):
+        raise ValueError(f"shape mismatch q{tuple(q8.shape)} k{tuple(k8.shape)} v{tuple(v8.shape)}")
+    if out is None:
+        out = torch.empty((B, S, Hq, dv), dtype=torch.bfloat16, device=q8.device)
+    elif out.dtype != torch.bfloat16 or tuple(out.shape) != (B, S, Hq, dv) or not out.is_contiguous():
+        raise ValueError("out must be a contiguous bf16 tensor of shape (B, S, Hq, d_v)")
+    sm = 0.0 if softmax_scale is None else float(softmax_scale)
+    st = attn_fwd_fp8_raw(q8.data_ptr(), k8.data_ptr(), v8.data_ptr(), out.data_ptr(),
+                          float(q_scale), float(k_scale), float(v_scale), sm,
+                          B, Hq, Hkv, S, dqk, dv, int(bool(causal)), _P_MODES[p_mode],
+                          _stream_ptr(stream, q8.device))
+    _check(st)
+    return out
+
+
+def attn_fwd_bf16(q, k, v, softmax_scale=None, causal=True, out=None, stream=None):
+    """Causal BF16 attention on bf16 (B,S,H,d) tensors; returns bf16 (B,S,Hq,d_v)."""
+    for t, n in ((q, "q"), (k, "k"), (v, "v")):
+        if t.dtype != torch.bfloat16:
+            raise TypeError(f"{n} must be bfloat16, got {t.dtype}")
+    B, S, Hq, dqk = _bshd(q, "q")
+    Bk, Sk, Hkv, dk = _bshd(k, "k")
+    Bv, Sv, Hv, dv = _bshd(v, "v")
+    if (Bk, Sk, dk) != (B, S, dqk) or (Bv, Sv, Hv) != (B, S, Hkv):
+        raise ValueError(f"shape mismatch q{tuple(q.shape)} k{tuple(k.shape)} v{tuple(v.shape)}")
+    if out is None:
+        out = torch.empty((B, S, Hq, dv), dtype=torch.bfloat16, device=q.device)
+    elif out.dtype != torch.bfloat16 or tuple(out.shape) != (B, S, Hq, dv) or not out.is_contiguous():
+        raise ValueError("out must be a contiguous bf16 tensor of shape (B, S, Hq, d_v)")
+    sm = 0.0 if softmax_scale is None else float(softmax_scale)
+    st = attn_fwd_bf16_raw(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), sm,
+                           B, Hq, Hkv, S, dqk, dv, int(bool(causal)), _stream_ptr(stream, q.device))
+    _check(st)
+    return out
+
+
+def causal_flops(B, Hq, S, d_qk, d_v):
+    """2*B*Hq*S^2*(d_qk+d_v)/2 - the causal FLOP count throughput is quoted in."""
+    return 2.0 * B * Hq * S * S * (d_qk + d_v) / 2.0
+
+
+def default_softmax_scale(d_qk):
+    return 1.0 / math.sqrt(d_qk)

@@ -1,0 +1,107 @@
+// C-ABI layer of libattnfwd.so: argument validation, defaults, dispatch and
+// error reporting.  Every check runs on the host before any HIP call.
+#include "../../include/attn_fwd.h"
+#include "launch.h"
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdint>
+#include <cstdio>
+
+namespace {
+
+thread_local char g_err[512] = {0};
+
+int fail(int status, const char* fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_err, sizeof(g_err), fmt, ap);
+    va_end(ap);
+    return status;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
+    uintptr_t a0 = reinterpret_cast<uintptr_t>(a), b0 = reinterpret_cast<uintptr_t>(b);
+    return a0 < b0 + nb && b0 < a0 + na;
+}
+
+// Shared checks; elem_qkv = bytes per Q/K/V element.  Returns ATTN_OK, an error,
+// or -1 for "empty problem, nothing to do".
+int check_common(const void* q, const void* k, const void* v, void* o, float softmax_scale,
+                 int B, int Hq, int Hkv, int S, int d_qk, int d_v, int causal, size_t elem_qkv,
+                 const char* who) {
+    if (B < 0 || S < 0) return fail(ATTN_E_INVALID_ARG, "%s: B=%d and S=%d must be >= 0", who, B, S);
+    if (Hq <= 0 || Hkv <= 0) return fail(ATTN_E_INVALID_ARG, "%s: Hq=%d and Hkv=%d must be >= 1", who, Hq, Hkv);
+    if (Hq % Hkv != 0) return fail(ATTN_E_INVALID_ARG, "%s: Hq=%d is not a multiple of Hkv=%d", who, Hq, Hkv);
+    if (d_qk <= 0 || d_v <= 0) return fail(ATTN_E_INVALID_ARG, "%s: head dims d_qk=%d d_v=%d must be > 0", who, d_qk, d_v);
+    if (!(std::isfinite(softmax_scale))) return fail(ATTN_E_INVALID_ARG, "%s: softmax_scale is not finite", who);
+    if (causal != 0 && causal != 1) return fail(ATTN_E_INVALID_ARG, "%s: causal=%d must be 0 or 1", who, causal);
+    if (d_qk != 128 && d_qk != 192) return fail(ATTN_E_UNSUPPORTED, "%s: d_qk=%d unsupported (128 or 192)", who, d_qk);
+    if (d_v != 128) return fail(ATTN_E_UNSUPPORTED, "%s: d_v=%d unsupported (128)", who, d_v);
+    if (causal != 1) return fail(ATTN_E_UNSUPPORTED, "%s: only causal attention is implemented", who);
+    // Every element offset is formed in 64-bit arithmetic by the kernels; the row
+    // index b*S+s and the head count must fit comfortably in 32-bit integers.
+    if ((int64_t)B * S > (int64_t)1 << 30) return fail(ATTN_E_UNSUPPORTED, "%s: B*S=%lld too large", who, (long long)B * S);
+    if (B == 0 || S == 0) return -1;
+    if (!q || !k || !v || !o) return fail(ATTN_E_INVALID_ARG, "%s: null tensor pointer", who);
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o))
+        return fail(ATTN_E_INVALID_ARG, "%s: tensor pointers must be 16-byte aligned", who);
+    const size_t nq = (size_t)B * S * Hq * d_qk * elem_qkv;
+    const size_t nk = (size_t)B * S * Hkv * d_qk * elem_qkv;
+    const size_t nv = (size_t)B * S * Hkv * d_v * elem_qkv;
+    const size_t no = (size_t)B * S * Hq * d_v * 2;
+    if (overlaps(o, no, q, nq) || overlaps(o, no, k, nk) || overlaps(o, no, v, nv))
+        return fail(ATTN_E_INVALID_ARG, "%s: output overlaps an input", who);
+    return ATTN_OK;
+}
+
+int finish(hipError_t e, const char* who) {
+    if (e != hipSuccess) return fail(ATTN_E_HIP, "%s: HIP error %d (%s)", who, (int)e, hipGetErrorString(e));
+    g_err[0] = 0;
+    return ATTN_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int attn_fwd_fp8(const void* q, const void* k, const void* v, void* o,
+                 float q_scale, float k_scale, float v_scale, float softmax_scale,
+                 int B, int Hq, int Hkv, int S, int d_qk, int d_v,
+                 int causal, int p_mode, hipStream_t stream) {
+    const char* who = "attn_fwd_fp8";
+    int st = check_common(q, k, v, o, softmax_scale, B, Hq, Hkv, S, d_qk, d_v, causal, 1, who);
+    if (st == -1) { g_err[0] = 0; return ATTN_OK; }
+    if (st != ATTN_OK) return st;
+    if (!(std::isfinite(q_scale) && q_scale > 0.f) || !(std::isfinite(k_scale) && k_scale > 0.f) ||
+        !(std::isfinite(v_scale) && v_scale > 0.f))
+        return fail(ATTN_E_INVALID_ARG, "%s: q/k/v scales must be finite and > 0", who);
+    if (p_mode != ATTN_P_EXACT && p_mode != ATTN_P_LEAN)
+        return fail(ATTN_E_INVALID_ARG, "%s: p_mode=%d must be 0 (exact) or 1 (lean)", who, p_mode);
+    attnfwd::Problem p{q, k, v, o, q_scale, k_scale, v_scale,
+                       softmax_scale > 0.f ? softmax_scale : 1.0f / std::sqrt((float)d_qk),
+                       B, Hq, Hkv, S, d_qk, d_v, p_mode, stream};
+    const double c = (double)q_scale * k_scale * p.sm * 1.4426950408889634;
+    if (!(c < 1e30 && c > 1e-30)) return fail(ATTN_E_INVALID_ARG, "%s: q_scale*k_scale*softmax_scale out of range", who);
+    return finish(attnfwd::launch_fp8(p), who);
+}
+
+int attn_fwd_bf16(const void* q, const void* k, const void* v, void* o, float softmax_scale,
+                  int B, int Hq, int Hkv, int S, int d_qk, int d_v, int causal, hipStream_t stream) {
+    const char* who = "attn_fwd_bf16";
+    int st = check_common(q, k, v, o, softmax_scale, B, Hq, Hkv, S, d_qk, d_v, causal, 2, who);
+    if (st == -1) { g_err[0] = 0; return ATTN_OK; }
+    if (st != ATTN_OK) return st;
+    attnfwd::Problem p{q, k, v, o, 1.f, 1.f, 1.f,
+                       softmax_scale > 0.f ? softmax_scale : 1.0f / std::sqrt((float)d_qk),
+                       B, Hq, Hkv, S, d_qk, d_v, 0, stream};
+    return finish(attnfwd::launch_bf16(p), who);
+}
+
+const char* attn_last_error(void) { return g_err; }
+
+int attn_abi_version(void) { return 100; }
+
+}  // extern "C"

@@ -1,0 +1,349 @@
+// FP8 (OCP e4m3fn) causal prefill attention for gfx950.
+//
+// Method: "Zyphra ZYFA: FP8 FlashAttention for AMD MI355X, Up to 1.76x Faster"
+// (MarkTechPost), sections "Lean P: one multiply-add instead of an exponential"
+// and "Per-block scaling and a rounded row sum"; "Breaking the FP8 Attention
+// Bottleneck on AMD MI355X" (kg.zhiyong.dev), section "ZYFA's Technical
+// Solutions".  Per query row and 64-key block:
+//   s   = <Q8_i, K8_j> on the FP8 matrix cores (fp32 accumulate)
+//   t   = s * c,  c = q_scale * k_scale * sm * log2(e)        (log2-domain score)
+//   M   = ceil(max_j t)                                         (block exponent)
+//   p~  = e4m3(2^(t - M + 8))   exact path: v_exp_f32 + RNE convert
+//       = byte rint(8c*s + 120 - 8M) clamped to [0,255]        Lean P: FMA + convert
+//   O  += 2^(M-8-R) * p~ . V8   scaled MFMA, the power of two is the E8M0 B scale
+//   L  += 2^(M-8-R) * sum p~    one more scaled MFMA against an all-ones operand
+//   out = bf16(v_scale * (O / L))
+// R is a per-row power-of-two reference that only moves (with an exact
+// rescale of O and L) when a block exponent exceeds it by more than 16.
+//
+// Mapping on CDNA4.  A workgroup is NW waves; each wave owns 32 consecutive
+// query rows of one head and walks the causal key blocks.  The score tile is
+// computed transposed, S^T = K . Q^T (v_mfma_f32_32x32x64_f8f6f4, A = K rows
+// from LDS, B = the wave's Q held in registers), so lane l holds query l%32 and
+// 32 of the block's 64 keys: the row max is 32 in-lane maxima plus one
+// v_permlane32_swap, and the packed FP8 probabilities are already the B operand
+// of O^T = V^T . P^T.  V^T comes straight from LDS with the transposing
+// ds_read_b64_tr_b8.  K and V blocks are staged HBM -> registers -> LDS with
+// 16-byte coalesced loads, double-buffered, one barrier per block.
+#include "common.h"
+#include "launch.h"
+
+namespace attnfwd {
+namespace {
+
+constexpr int KB = 64;               // keys per block = the probability scaling block
+constexpr float kRefSlack = 16.0f;   // move the reference only if a block exceeds it by more
+
+template <int DQK>
+struct Fp8Tile {
+    static constexpr int NKK = DQK / 64;          // 32x32x64 steps over d_qk
+    static constexpr int K_STRIDE = DQK + 16;     // padded LDS row of K, bytes
+    static constexpr int K_BYTES = KB * K_STRIDE;
+    static constexpr int V_BYTES = KB * 128;      // d_v = 128 bytes per key, chunk-swizzled
+    static constexpr int STAGE = K_BYTES + V_BYTES;
+    static constexpr int K_CHUNKS = KB * DQK / 16;
+    static constexpr int V_CHUNKS = KB * 128 / 16;
+};
+
+struct Fp8Params {
+    const uint8_t* q;
+    const uint8_t* k;
+    const uint8_t* v;
+    __bf16* o;
+    float c;        // q_scale * k_scale * sm * log2(e)
+    float a8;       // 8 * c, the Lean-P slope
+    float v_scale;
+    int B, Hq, Hkv, S;
+    int n_tiles;    // query tiles per head
+};
+
+// 16-byte chunk swizzle of a V row in LDS.  The transposing read of one 16-lane
+// group touches keys {b..b+3, b+8..b+11} (b = 0 mod 4); this maps them to 8
+// distinct chunk positions, so the group's 128 bytes hit distinct banks.
+__device__ __forceinline__ int v_swz(int row) { return (row & 3) | (((row >> 3) & 1) << 2); }
+
+template <int DQK, int NW, int PMODE>
+__global__ void __launch_bounds__(NW * 64) fp8_causal_fwd(Fp8Params a) {
+    using T = Fp8Tile<DQK>;
+    constexpr int NT = NW * 64;
+    constexpr int BM = NW * 32;
+    constexpr int KPT = (T::K_CHUNKS + NT - 1) / NT;
+    constexpr int VPT = (T::V_CHUNKS + NT - 1) / NT;
+    constexpr int KCH_ROW = DQK / 16;
+
+    __shared__ __attribute__((aligned(16))) uint8_t smem_raw[2 * T::STAGE];
+    ATTN_LDS uint8_t* smem = (ATTN_LDS uint8_t*)smem_raw;
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int w = tid >> 6;
+    const int BH = a.B * a.Hq;
+    const int L = blockIdx.x;
+    const int tile = a.n_tiles - 1 - L / BH;      // heaviest (longest causal prefix) tiles first
+    const int bh = L % BH;                        // consecutive blocks: consecutive heads (XCD spread)
+    const int b = bh / a.Hq;
+    const int h = bh - b * a.Hq;
+    const int g = h / (a.Hq / a.Hkv);
+    const int S = a.S;
+    const int q0 = tile * BM;
+    const int qw0 = q0 + 32 * w;
+    const int kend = min(S, q0 + BM);
+    const int nblk = (kend + KB - 1) / KB;                         // key blocks the workgroup stages
+    const int wnblk = qw0 < S ? (min(qw0 + 31, S - 1) / KB + 1) : 0;  // key blocks this wave uses
+
+    const int c = lane & 31;
+    const int hh = lane >> 5;
+    const int qabs = qw0 + c;
+
+    const int64_t q_row = (int64_t)a.Hq * DQK;
+    const int64_t k_row = (int64_t)a.Hkv * DQK;
+    const int64_t v_row = (int64_t)a.Hkv * 128;
+    const uint8_t* kbase = a.k + (int64_t)b * S * k_row + (int64_t)g * DQK;
+    const uint8_t* vbase = a.v + (int64_t)b * S * v_row + (int64_t)g * 128;
+
+    // Q^T operand: lane (query c, half hh) holds d in [64kk + 32hh, +32) for each step kk.
+    i32x8 qreg[T::NKK];
+    {
+        const bool ok = qabs < S;
+        const uint8_t* qp = a.q + ((int64_t)b * S + (ok ? qabs : 0)) * q_row + (int64_t)h * DQK + 32 * hh;
+#pragma unroll
+        for (int kk = 0; kk < T::NKK; ++kk) {
+            i32x4 lo = ok ? load16(qp + 64 * kk) : i32x4{0, 0, 0, 0};
+            i32x4 hi = ok ? load16(qp + 64 * kk + 16) : i32x4{0, 0, 0, 0};
+            qreg[kk] = i32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+        }
+    }
+
+    i32x4 kst[KPT];
+    i32x4 vst[VPT];
+    auto gload = [&](int j) {
+#pragma unroll
+        for (int i = 0; i < KPT; ++i) {
+            const int idx = tid + i * NT;
+            if (T::K_CHUNKS % NT == 0 || idx < T::K_CHUNKS) {
+                const int row = idx / KCH_ROW, cc = idx % KCH_ROW;
+                const int key = j * KB + row;
+                kst[i] = key < S ? load16(kbase + key * k_row + 16 * cc) : i32x4{0, 0, 0, 0};
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < VPT; ++i) {
+            const int idx = tid + i * NT;
+            if (T::V_CHUNKS % NT == 0 || idx < T::V_CHUNKS) {
+                const int row = idx >> 3, cc = idx & 7;
+                const int key = j * KB + row;
+                vst[i] = key < S ? load16(vbase + key * v_row + 16 * cc) : i32x4{0, 0, 0, 0};
+            }
+        }
+    };
+    auto lstore = [&](int st) {
+        ATTN_LDS uint8_t* Ks = smem + st * T::STAGE;
+        ATTN_LDS uint8_t* Vs = Ks + T::K_BYTES;
+#pragma unroll
+        for (int i = 0; i < KPT; ++i) {
+            const int idx = tid + i * NT;
+            if (T::K_CHUNKS % NT == 0 || idx < T::K_CHUNKS) {
+                const int row = idx / KCH_ROW, cc = idx % KCH_ROW;
+                lds_store16(Ks + row * T::K_STRIDE + 16 * cc, kst[i]);
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < VPT; ++i) {
+            const int idx = tid + i * NT;
+            if (T::V_CHUNKS % NT == 0 || idx < T::V_CHUNKS) {
+                const int row = idx >> 3, cc = idx & 7;
+                lds_store16(Vs + row * 128 + 16 * (cc ^ v_swz(row)), vst[i]);
+            }
+        }
+    };
+
+    // Per-lane offsets of the transposing V reads: group G = lane/16 reads rows
+    // (keys) of chunk cc in the order of the probability bytes, columns
+    // 32dt + 16(G&1) + [0,16).
+    int voff[4];
+    {
+        const int G = lane >> 4, i = lane & 15, k = i >> 1;
+#pragma unroll
+        for (int cc = 0; cc < 4; ++cc) {
+            const int key = 32 * (cc >> 1) + 16 * (cc & 1) + 8 * (k >> 2) + 4 * hh + (k & 3);
+            voff[cc] = key * 128 + 8 * (i & 1) + 16 * ((G & 1) ^ v_swz(key));
+        }
+    }
+    // The chunk of d-tile dt is 2dt + (G&1); since 2dt and G&1 share no bits,
+    // 16*((2dt + (G&1)) ^ s) == (32*dt) ^ (16*((G&1) ^ s)), so the tile offset is
+    // applied below as voff ^ (32*dt) (bits 5-6, disjoint from key*128 and 8*(i&1)).
+
+    f32x16 o[4];
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt) o[dt] = f32x16{0};
+    f32x16 lacc = f32x16{0};
+    float ref = -INFINITY;
+    const i32x8 ones = i32x8{0x38383838, 0x38383838, 0x38383838, 0x38383838,
+                             0x38383838, 0x38383838, 0x38383838, 0x38383838};
+
+    gload(0);
+    lstore(0);
+    __syncthreads();
+
+    for (int j = 0; j < nblk; ++j) {
+        const int st = j & 1;
+        if (j + 1 < nblk) gload(j + 1);
+        if (j < wnblk) {
+            const ATTN_LDS uint8_t* Ks = smem + st * T::STAGE;
+            const ATTN_LDS uint8_t* Vs = Ks + T::K_BYTES;
+
+            // ---- S^T = K . Q^T for keys [0,32) and [32,64) of the block
+            f32x16 s0 = f32x16{0}, s1 = f32x16{0};
+#pragma unroll
+            for (int kk = 0; kk < T::NKK; ++kk) {
+                const ATTN_LDS uint8_t* kp = Ks + c * T::K_STRIDE + 64 * kk + 32 * hh;
+                i32x4 a0l = lds_load16(kp), a0h = lds_load16(kp + 16);
+                i32x4 a1l = lds_load16(kp + 32 * T::K_STRIDE), a1h = lds_load16(kp + 32 * T::K_STRIDE + 16);
+                i32x8 a0 = i32x8{a0l[0], a0l[1], a0l[2], a0l[3], a0h[0], a0h[1], a0h[2], a0h[3]};
+                i32x8 a1 = i32x8{a1l[0], a1l[1], a1l[2], a1l[3], a1h[0], a1h[1], a1h[2], a1h[3]};
+                s0 = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a0, qreg[kk], s0, 0, 0, 0, 0, 0, 0);
+                s1 = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a1, qreg[kk], s1, 0, 0, 0, 0, 0, 0);
+            }
+
+            // ---- causal / tail mask (only blocks that reach past the wave's first query)
+            const int kb0 = j * KB;
+            if (kb0 + KB - 1 > qw0) {
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int key = kb0 + 8 * (r >> 2) + 4 * hh + (r & 3);
+                    if (key > qabs || key >= S) s0[r] = -INFINITY;
+                    if (key + 32 > qabs || key + 32 >= S) s1[r] = -INFINITY;
+                }
+            }
+
+            // ---- block exponent M = ceil(max t)
+            float mx = -INFINITY;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) mx = fmaxf(mx, fmaxf(s0[r], s1[r]));
+            mx = fmaxf(mx, other_half(mx));
+            const float M = fmaxf(ceilf(mx * a.c), -1.0e30f);  // floor: rows with no visible key here
+
+            // ---- lazy power-of-two reference
+            const bool need = M > ref + kRefSlack;
+            if (__ballot(need)) {
+                const float nref = need ? M : ref;
+                const float f = need ? __builtin_amdgcn_exp2f(ref - nref) : 1.0f;
+#pragma unroll
+                for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) o[dt][r] *= f;
+#pragma unroll
+                for (int r = 0; r < 16; ++r) lacc[r] *= f;
+                ref = nref;
+            }
+            const int scale_b = (int)fminf(fmaxf(M - 8.0f - ref, -127.0f), 127.0f) + 127;
+
+            // ---- probabilities as e4m3 bytes, in B-operand order
+            int pw[8];
+            if (PMODE == 0) {
+                const float bias = 8.0f - M;
+#pragma unroll
+                for (int q4 = 0; q4 < 4; ++q4) {
+                    float p0 = __builtin_amdgcn_exp2f(fmaf(s0[4 * q4 + 0], a.c, bias));
+                    float p1 = __builtin_amdgcn_exp2f(fmaf(s0[4 * q4 + 1], a.c, bias));
+                    float p2 = __builtin_amdgcn_exp2f(fmaf(s0[4 * q4 + 2], a.c, bias));
+                    float p3 = __builtin_amdgcn_exp2f(fmaf(s0[4 * q4 + 3], a.c, bias));
+                    int wd = __builtin_amdgcn_cvt_pk_fp8_f32(p0, p1, 0, false);
+                    pw[q4] = __builtin_amdgcn_cvt_pk_fp8_f32(p2, p3, wd, true);
+                    p0 = __builtin_amdgcn_exp2f(fmaf(s1[4 * q4 + 0], a.c, bias));
+                    p1 = __builtin_amdgcn_exp2f(fmaf(s1[4 * q4 + 1], a.c, bias));
+                    p2 = __builtin_amdgcn_exp2f(fmaf(s1[4 * q4 + 2], a.c, bias));
+                    p3 = __builtin_amdgcn_exp2f(fmaf(s1[4 * q4 + 3], a.c, bias));
+                    wd = __builtin_amdgcn_cvt_pk_fp8_f32(p0, p1, 0, false);
+                    pw[4 + q4] = __builtin_amdgcn_cvt_pk_fp8_f32(p2, p3, wd, true);
+                }
+            } else {
+                const float bc = 120.0f - 8.0f * M;
+#pragma unroll
+                for (int q4 = 0; q4 < 4; ++q4) {
+                    unsigned wd = 0;
+                    wd = __builtin_amdgcn_cvt_pk_u8_f32(fmaf(s0[4 * q4 + 0], a.a8, bc), 0, wd);
+                    wd = __builtin_amdgcn_cvt_pk_u8_f32(fmaf(s0[4 * q4 + 1], a.a8, bc), 1, wd);
+                    wd = __builtin_amdgcn_cvt_pk_u8_f32(fmaf(s0[4 * q4 + 2], a.a8, bc), 2, wd);
+                    wd = __builtin_amdgcn_cvt_pk_u8_f32(fmaf(s0[4 * q4 + 3], a.a8, bc), 3, wd);
+                    pw[q4] = (int)wd;
+                    wd = 0;
+                    wd = __builtin_amdgcn_cvt_pk_u8_f32(fmaf(s1[4 * q4 + 0], a.a8, bc), 0, wd);
+                    wd = __builtin_amdgcn_cvt_pk_u8_f32(fmaf(s1[4 * q4 + 1], a.a8, bc), 1, wd);
+                    wd = __builtin_amdgcn_cvt_pk_u8_f32(fmaf(s1[4 * q4 + 2], a.a8, bc), 2, wd);
+                    wd = __builtin_amdgcn_cvt_pk_u8_f32(fmaf(s1[4 * q4 + 3], a.a8, bc), 3, wd);
+                    pw[4 + q4] = (int)wd;
+                }
+            }
+            const i32x8 pv = i32x8{pw[0], pw[1], pw[2], pw[3], pw[4], pw[5], pw[6], pw[7]};
+
+            // ---- O^T += V^T . P^T (scaled), L += 1 . P^T (scaled)
+#pragma unroll
+            for (int dt = 0; dt < 4; ++dt) {
+                i32x8 va;
+#pragma unroll
+                for (int cc = 0; cc < 4; ++cc) {
+                    i32x2 t = lds_read_tr8(Vs + (voff[cc] ^ (32 * dt)));
+                    va[2 * cc] = t[0];
+                    va[2 * cc + 1] = t[1];
+                }
+                o[dt] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(va, pv, o[dt], 0, 0, 0, 127, 0, scale_b);
+            }
+            lacc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(ones, pv, lacc, 0, 0, 0, 127, 0, scale_b);
+        }
+        if (j + 1 < nblk) lstore(st ^ 1);
+        __syncthreads();
+    }
+
+    // ---- epilogue: out = bf16(v_scale * (O / L)), lane holds query c, d = 32dt + 8(r/4) + 4hh + r%4
+    if (qabs < S && wnblk > 0) {
+        const float lsum = lacc[0];
+        __bf16* op = a.o + (((int64_t)b * S + qabs) * a.Hq + h) * 128;
+#pragma unroll
+        for (int dt = 0; dt < 4; ++dt) {
+#pragma unroll
+            for (int r4 = 0; r4 < 4; ++r4) {
+                float x0 = (o[dt][4 * r4 + 0] / lsum) * a.v_scale;
+                float x1 = (o[dt][4 * r4 + 1] / lsum) * a.v_scale;
+                float x2 = (o[dt][4 * r4 + 2] / lsum) * a.v_scale;
+                float x3 = (o[dt][4 * r4 + 3] / lsum) * a.v_scale;
+                uint2 pk = make_uint2(pack_bf16x2(x0, x1), pack_bf16x2(x2, x3));
+                *reinterpret_cast<uint2*>(op + 32 * dt + 8 * r4 + 4 * hh) = pk;
+            }
+        }
+    }
+}
+
+template <int DQK, int NW, int PMODE>
+hipError_t launch_t(const Problem& p) {
+    constexpr int BM = NW * 32;
+    Fp8Params a;
+    a.q = static_cast<const uint8_t*>(p.q);
+    a.k = static_cast<const uint8_t*>(p.k);
+    a.v = static_cast<const uint8_t*>(p.v);
+    a.o = static_cast<__bf16*>(p.o);
+    const double c = (double)p.q_scale * p.k_scale * p.sm * 1.4426950408889634;
+    a.c = (float)c;
+    a.a8 = (float)(8.0 * c);
+    a.v_scale = p.v_scale;
+    a.B = p.B;
+    a.Hq = p.Hq;
+    a.Hkv = p.Hkv;
+    a.S = p.S;
+    a.n_tiles = (p.S + BM - 1) / BM;
+    const long long nblocks = (long long)a.n_tiles * p.B * p.Hq;
+    if (nblocks <= 0 || nblocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+    hipLaunchKernelGGL((fp8_causal_fwd<DQK, NW, PMODE>), dim3((unsigned)nblocks), dim3(NW * 64), 0, p.stream, a);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_fp8(const Problem& p) {
+    constexpr int NW = 4;
+    if (p.d_qk == 128) return p.p_mode == 0 ? launch_t<128, NW, 0>(p) : launch_t<128, NW, 1>(p);
+    if (p.d_qk == 192) return p.p_mode == 0 ? launch_t<192, NW, 0>(p) : launch_t<192, NW, 1>(p);
+    return hipErrorInvalidValue;
+}
+
+}  // namespace attnfwd

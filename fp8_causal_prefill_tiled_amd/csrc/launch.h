@@ -1,0 +1,24 @@
+// Internal interface between the C-ABI layer (api.cpp) and the kernel launchers.
+#pragma once
+#include <hip/hip_runtime_api.h>
+#include <stdint.h>
+
+namespace attnfwd {
+
+// A validated problem.  Shapes follow include/attn_fwd.h; sm is the final
+// softmax scale (already defaulted to 1/sqrt(d_qk)).
+struct Problem {
+    const void* q;
+    const void* k;
+    const void* v;
+    void* o;
+    float q_scale, k_scale, v_scale, sm;
+    int B, Hq, Hkv, S, d_qk, d_v;
+    int p_mode;
+    hipStream_t stream;
+};
+
+hipError_t launch_fp8(const Problem& p);
+hipError_t launch_bf16(const Problem& p);
+
+}  // namespace attnfwd

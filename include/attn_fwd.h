@@ -1,0 +1,115 @@
+/*
+ * attn_fwd.h - C ABI of libattnfwd.so: causal forward prefill attention on
+ * AMD Instinct MI355X (CDNA4, gfx950).
+ *
+ * Operation (both entry points): for every batch b, query head h and query
+ * position i < S,
+ *
+ *     O[b,i,h,:] = sum_{j<=i} softmax_j( sm * <Q[b,i,h,:], K[b,j,g,:]> ) * V[b,j,g,:]
+ *
+ * with g = h / (Hq / Hkv) (grouped-query attention by consecutive groups) and
+ * sm the softmax scale.  This is the causal, equal-length forward prefill the
+ * pages scope the kernels to ("Breaking the FP8 Attention Bottleneck on AMD
+ * MI355X: How Zyphra ZYFA Unleashes Performance", section "Application
+ * Boundaries and Engineering Decisions"; "Zyphra ZYFA: FP8 FlashAttention for
+ * AMD MI355X, Up to 1.76x Faster", TL;DR and comparison table row "Scope"),
+ * computed FlashAttention-style as an online softmax over 64-key blocks.
+ *
+ * Layout: every tensor is contiguous (B, S, H, d) - the flash_attn_func
+ * convention ("drop-in flash_attn_func interface", TL;DR of the second page).
+ * Q: (B,S,Hq,d_qk), K: (B,S,Hkv,d_qk), V: (B,S,Hkv,d_v), O: (B,S,Hq,d_v) bf16.
+ *
+ * Ownership and execution: all pointers are device pointers owned by the
+ * caller; the library keeps no state, allocates nothing and is reentrant.
+ * The call enqueues its kernels on `stream` (0 = the default stream) and
+ * returns without synchronising; O is valid once the stream has completed.
+ * O must not overlap Q, K or V.
+ *
+ * Supported shapes: d_qk in {128, 192}, d_v == 128, Hq % Hkv == 0, S >= 1
+ * (any S; the ragged last tile is masked), causal == 1, pointers 16-byte
+ * aligned.  B == 0 or S == 0 is an empty problem: ATTN_OK, nothing launched.
+ *
+ * Errors: every argument check happens on the host before any HIP call and
+ * returns ATTN_E_INVALID_ARG (a malformed argument) or ATTN_E_UNSUPPORTED (a
+ * well-formed request outside the supported set); a launch failure returns
+ * ATTN_E_HIP.  The library never aborts and never writes errno.
+ * attn_last_error() describes the last non-OK status of the calling thread.
+ */
+#ifndef ATTN_FWD_H
+#define ATTN_FWD_H
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    ATTN_OK = 0,
+    ATTN_E_INVALID_ARG = 1,
+    ATTN_E_UNSUPPORTED = 2,
+    ATTN_E_HIP = 3
+} attn_status;
+
+/* Probability path of the FP8 kernel. */
+typedef enum {
+    /* p = e4m3_RNE(2^(t - M + 8)) from a true exponential on the vector unit
+     * (the "exact P" of "Zyphra ZYFA: FP8 FlashAttention...", section
+     * "Two-wave ping-pong schedule"). */
+    ATTN_P_EXACT = 0,
+    /* Lean P: the e4m3 code of 2^x is about 8x + 56, so the probability's FP8
+     * byte is one multiply-add and one round-to-integer ("Zyphra ZYFA: FP8
+     * FlashAttention...", section "Lean P: one multiply-add instead of an
+     * exponential"). */
+    ATTN_P_LEAN = 1
+} attn_p_mode;
+
+/*
+ * FP8 causal prefill attention.
+ *
+ * q, k, v: OCP e4m3fn bytes; the dequantised value is scale * decode(byte)
+ *          with q_scale, k_scale, v_scale > 0 and finite (per-tensor scales).
+ * o:       bfloat16 output (round to nearest even).
+ * softmax_scale: sm; a value <= 0 selects 1/sqrt(d_qk).
+ * p_mode:  attn_p_mode.
+ *
+ * Method ("Zyphra ZYFA: FP8 FlashAttention for AMD MI355X, Up to 1.76x
+ * Faster", section "Per-block scaling and a rounded row sum"): per query row
+ * and 64-key block the probabilities are taken relative to 2^(M-8), M the
+ * ceiling of the block's largest log2-domain score, rounded to e4m3, and
+ * multiplied into V by the block-scaled FP8 matrix instruction whose E8M0
+ * operand scale restores the power of two; the row is normalised by the sum
+ * of the rounded probabilities (one extra matrix instruction per block).
+ */
+int attn_fwd_fp8(const void* q, const void* k, const void* v, void* o,
+                 float q_scale, float k_scale, float v_scale, float softmax_scale,
+                 int B, int Hq, int Hkv, int S, int d_qk, int d_v,
+                 int causal, int p_mode, hipStream_t stream);
+
+/*
+ * BF16 causal prefill attention (the BF16 kernel of "Zyphra ZYFA: FP8
+ * FlashAttention...", section "What is ZYFA?").
+ *
+ * q, k, v: bfloat16; o: bfloat16.  softmax_scale <= 0 selects 1/sqrt(d_qk).
+ * Probabilities are fp32 exponentials relative to a running per-row power-of-
+ * two reference, rounded to bf16 for the P.V product; the row sum adds the
+ * unrounded fp32 probabilities (standard FlashAttention-2 normalisation; the
+ * pages do not describe the BF16 internals).
+ */
+int attn_fwd_bf16(const void* q, const void* k, const void* v, void* o,
+                  float softmax_scale,
+                  int B, int Hq, int Hkv, int S, int d_qk, int d_v,
+                  int causal, hipStream_t stream);
+
+/* Message for the calling thread's last non-OK status ("" if none).  The
+ * returned storage is thread-local and valid until that thread's next call. */
+const char* attn_last_error(void);
+
+/* ABI version of this header (major * 100 + minor). */
+int attn_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ATTN_FWD_H */

@@ -1,0 +1,97 @@
+"""The C-ABI library loads, exports every entry point include/attn_fwd.h declares,
+and rejects every malformed or unsupported request on the host, before any HIP
+call (so these run without a GPU)."""
+import math
+import os
+import re
+
+import pytest
+
+from fp8_causal_prefill_tiled_amd import binding
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+OK, INVALID, UNSUPPORTED = binding.ATTN_OK, binding.ATTN_E_INVALID_ARG, binding.ATTN_E_UNSUPPORTED
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(binding.library_path()):
+        from fp8_causal_prefill_tiled_amd import build
+        build.build()
+    return binding.load_library()
+
+
+def declared_functions():
+    names = set()
+    for fn in os.listdir(os.path.join(ROOT, "include")):
+        if fn.endswith(".h"):
+            text = open(os.path.join(ROOT, "include", fn)).read()
+            text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+            names |= set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(attn_\w+)\s*\(", text, flags=re.M))
+    return names
+
+
+def test_exports_every_declared_symbol(lib):
+    decl = declared_functions()
+    assert {"attn_fwd_fp8", "attn_fwd_bf16", "attn_last_error", "attn_abi_version"} <= decl
+    assert decl <= binding.exported_symbols()
+    assert lib.attn_abi_version() == 100
+
+
+# fake, never-dereferenced, 16-byte aligned device addresses of disjoint buffers
+Q, K, V, O = 0x10000000, 0x20000000, 0x30000000, 0x40000000
+
+
+def fp8(**kw):
+    a = dict(q=Q, k=K, v=V, o=O, q_scale=1.0, k_scale=1.0, v_scale=1.0, softmax_scale=0.0,
+             B=1, Hq=4, Hkv=2, S=128, d_qk=128, d_v=128, causal=1, p_mode=0)
+    a.update(kw)
+    return binding.attn_fwd_fp8_raw(**a)
+
+
+def bf16(**kw):
+    a = dict(q=Q, k=K, v=V, o=O, softmax_scale=0.0, B=1, Hq=4, Hkv=2, S=128, d_qk=128, d_v=128, causal=1)
+    a.update(kw)
+    return binding.attn_fwd_bf16_raw(**a)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=0), INVALID), (dict(o=0), INVALID), (dict(v=0), INVALID),
+    (dict(Hq=3), INVALID), (dict(Hkv=0), INVALID), (dict(S=-1), INVALID), (dict(B=-2), INVALID),
+    (dict(d_qk=64), UNSUPPORTED), (dict(d_qk=0), INVALID), (dict(d_v=192), UNSUPPORTED),
+    (dict(causal=0), UNSUPPORTED), (dict(causal=2), INVALID),
+    (dict(p_mode=2), INVALID), (dict(p_mode=-1), INVALID),
+    (dict(q_scale=0.0), INVALID), (dict(k_scale=-1.0), INVALID), (dict(v_scale=math.nan), INVALID),
+    (dict(v_scale=math.inf), INVALID), (dict(softmax_scale=math.nan), INVALID),
+    (dict(q_scale=1e-30, k_scale=1e-30), INVALID),
+    (dict(q=Q + 8), INVALID), (dict(o=O + 2), INVALID),
+    (dict(o=Q + 4096), INVALID),                      # output overlaps Q
+    (dict(S=0, q=0, k=0, v=0, o=0), OK), (dict(B=0, q=0, k=0, v=0, o=0), OK),  # empty: nothing launched
+])
+def test_fp8_host_validation(lib, kw, status):
+    assert fp8(**kw) == status
+    msg = binding.attn_last_error()
+    assert (msg == "") == (status == OK)
+    if status != OK:
+        assert msg.startswith("attn_fwd_fp8")
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(k=0), INVALID), (dict(Hq=5, Hkv=2), INVALID), (dict(d_qk=256), UNSUPPORTED),
+    (dict(causal=0), UNSUPPORTED), (dict(softmax_scale=math.inf), INVALID), (dict(k=K + 1), INVALID),
+    (dict(o=V + 64), INVALID), (dict(S=0, q=0, k=0, v=0, o=0), OK),
+])
+def test_bf16_host_validation(lib, kw, status):
+    assert bf16(**kw) == status
+    assert (binding.attn_last_error() == "") == (status == OK)
+
+
+def test_python_binding_rejects_bad_tensors(lib):
+    import torch
+    x = torch.zeros((1, 8, 2, 128), dtype=torch.uint8)
+    with pytest.raises(ValueError, match="GPU tensor"):
+        binding.attn_fwd_fp8(x, x, x, 1.0, 1.0, 1.0)
+    with pytest.raises(TypeError):
+        binding.attn_fwd_fp8(x.float(), x, x, 1.0, 1.0, 1.0)
+    with pytest.raises(TypeError):
+        binding.attn_fwd_bf16(x, x, x)

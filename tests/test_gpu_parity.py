@@ -1,0 +1,137 @@
+"""GPU parity of the HIP kernels (through the C ABI) against the CPU oracle.
+
+Full tensors at sizes the oracle finishes in seconds (several query tiles and
+key blocks, ragged tails, GQA, both head-dim shapes, edge sizes), bit-exact
+special cases, run-to-run determinism, and the full-size workloads in the launch
+configuration the benchmark times, compared on sampled rows.
+"""
+import hashlib
+
+import numpy as np
+import pytest
+import torch
+
+from parity import (W, binding, check_fp8, gpu_select, oracle_bf16, oracle_fp8, rel_rms,
+                    row0_expected_fp8, run_bf16, run_fp8, TOL_BF16)
+from oracle.e4m3 import bf16_rne, decode_e4m3
+
+pytestmark = pytest.mark.gpu
+MODES = ["exact", "lean"]
+
+
+def custom(B, Hq, Hkv, S, dqk, seed=1234):
+    return W.Workload(f"custom_B{B}_H{Hq}x{Hkv}_S{S}_d{dqk}", B, Hq, Hkv, S, dqk, 128)
+
+
+@pytest.mark.parametrize("mode", MODES)
+def test_tiny_full_tensor(mode):
+    w = W.WORKLOADS["tiny"]
+    d = W.make_fp8(w)
+    out = run_fp8(d, mode)
+    got = gpu_select(out)
+    emu, ref = oracle_fp8(d, mode)
+    check_fp8(got, emu, ref, f"tiny {mode}")
+    # row 0 has a single visible key: bit-exact
+    exp0 = row0_expected_fp8(d)
+    assert np.array_equal(got[:, 0].astype(np.float32), exp0), "row 0 not bit-exact"
+
+
+@pytest.mark.parametrize("mode", MODES)
+@pytest.mark.parametrize("shape", [
+    (1, 2, 2, 1, 128), (1, 2, 1, 2, 128), (1, 2, 2, 63, 128), (1, 2, 2, 64, 128), (1, 2, 2, 65, 128),
+    (2, 4, 2, 129, 128), (1, 4, 1, 200, 192), (1, 2, 2, 333, 128), (2, 4, 4, 515, 192),
+    (1, 8, 2, 1000, 128),
+])
+def test_ragged_and_gqa_full_tensor(shape, mode):
+    B, Hq, Hkv, S, dqk = shape
+    w = custom(B, Hq, Hkv, S, dqk)
+    d = W.make_fp8(w, seed=777 + S)
+    out = run_fp8(d, mode)
+    got = gpu_select(out)
+    emu, ref = oracle_fp8(d, mode)
+    check_fp8(got, emu, ref, f"{w.name} {mode}")
+    assert np.array_equal(got[:, 0].astype(np.float32), row0_expected_fp8(d)[:, np.arange(Hq) // (Hq // Hkv)])
+
+
+@pytest.mark.parametrize("mode", MODES)
+def test_zero_query_is_prefix_mean(mode):
+    w = custom(1, 2, 2, 300, 128)
+    d = W.make_fp8(w, seed=5)
+    d["q8"] = torch.zeros_like(d["q8"])
+    got = gpu_select(run_fp8(d, mode))
+    vd = decode_e4m3(d["v8"].numpy())
+    pm = d["v_scale"] * np.cumsum(vd, axis=1) / np.arange(1, 301)[None, :, None, None]
+    # all p~ = 256 -> exact weights; only fp32 accumulation order and bf16 output rounding remain
+    assert np.max(np.abs(got - pm) / (np.abs(pm) + 1e-3)) < 2 ** -7
+
+
+def test_empty_problem_launches_nothing():
+    z = torch.zeros((1, 0, 2, 128), dtype=torch.uint8, device="cuda:0")
+    out = binding.attn_fwd_fp8(z, z, z, 1.0, 1.0, 1.0)
+    assert out.shape == (1, 0, 2, 128)
+
+
+@pytest.mark.parametrize("mode", MODES)
+def test_deterministic_over_repeated_launches(mode):
+    w = custom(1, 8, 8, 4096, 128)
+    d = W.make_fp8(w, seed=99)
+    q8, k8, v8 = (d[n].to("cuda:0") for n in ("q8", "k8", "v8"))
+    out = torch.empty((1, 4096, 8, 128), dtype=torch.bfloat16, device="cuda:0")
+    digests = set()
+    for _ in range(30):
+        binding.attn_fwd_fp8(q8, k8, v8, d["q_scale"], d["k_scale"], d["v_scale"], p_mode=mode, out=out)
+        torch.cuda.synchronize()
+        digests.add(hashlib.sha256(out.view(torch.uint8).cpu().numpy().tobytes()).hexdigest())
+    assert len(digests) == 1
+
+
+def _sampled_heads(Hq):
+    return sorted({0, 1, Hq // 2, Hq - 1})
+
+
+@pytest.mark.parametrize("name,mode", [("gauss32k", "exact"), ("gauss32k", "lean"), ("mistral", "exact"),
+                                       ("mistral", "lean"), ("qwen", "lean"), ("mla", "exact"), ("mla", "lean")])
+def test_full_size_workloads_sampled(name, mode):
+    w = W.WORKLOADS[name]
+    d = W.make_fp8(w)
+    out = run_fp8(d, mode)
+    rows = W.sample_rows(w.S, 48).numpy()
+    heads = _sampled_heads(w.Hq)
+    got = gpu_select(out, heads=heads, rows=rows)
+    emu, ref = oracle_fp8(d, mode, heads=heads, rows=rows)
+    check_fp8(got, emu, ref, f"{name} {mode} (rows={len(rows)}, heads={heads})")
+    assert np.array_equal(got[:, 0].astype(np.float32),
+                          row0_expected_fp8(d)[:, np.array(heads) // (w.Hq // w.Hkv)])
+    # every output finite, not only the sampled ones
+    assert bool(torch.isfinite(out).all())
+
+
+# ----------------------------------------------------------------------------- BF16
+
+@pytest.mark.parametrize("shape", [(1, 2, 2, 256, 128), (2, 4, 2, 129, 128), (1, 4, 1, 333, 192),
+                                   (1, 2, 2, 1, 128), (1, 2, 2, 65, 192)])
+def test_bf16_full_tensor(shape):
+    B, Hq, Hkv, S, dqk = shape
+    d = W.make_bf16(custom(B, Hq, Hkv, S, dqk), seed=31 + S)
+    got = gpu_select(run_bf16(d))
+    ref = oracle_bf16(d)
+    e = rel_rms(got, ref)
+    print(f"[parity] bf16 {shape}: vs fp64 {e:.2e}")
+    assert np.all(np.isfinite(got)) and e <= TOL_BF16
+    # row 0: O_0 = v_0 * bf16(p)/p, within one bf16 ulp of v_0
+    v0 = d["v"][:, 0].float().numpy()[:, np.arange(Hq) // (Hq // Hkv)]
+    assert np.all(np.abs(got[:, 0] - v0) <= 2.0 ** -7 * np.abs(v0) + 1e-30)
+
+
+@pytest.mark.parametrize("name", ["qwen", "mla"])
+def test_bf16_full_size_sampled(name):
+    w = W.WORKLOADS[name]
+    d = W.make_bf16(w)
+    out = run_bf16(d)
+    rows = W.sample_rows(w.S, 48).numpy()
+    heads = _sampled_heads(w.Hq)
+    got = gpu_select(out, heads=heads, rows=rows)
+    ref = oracle_bf16(d, heads=heads, rows=rows)
+    e = rel_rms(got, ref)
+    print(f"[parity] bf16 {name}: vs fp64 {e:.2e}")
+    assert e <= TOL_BF16 and bool(torch.isfinite(out).all())
