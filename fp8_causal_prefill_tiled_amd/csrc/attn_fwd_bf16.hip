@@ -286,7 +286,7 @@ hipError_t launch_t(const Problem& p) {
 }  // namespace
 
 hipError_t launch_bf16(const Problem& p) {
-    constexpr int NW = 4;
+    constexpr int NW = 8;
     if (p.d_qk == 128) return launch_t<128, NW>(p);
     if (p.d_qk == 192) return launch_t<192, NW>(p);
     return hipErrorInvalidValue;

@@ -205,14 +205,16 @@ __global__ void __launch_bounds__(NW * 64) fp8_causal_fwd(Fp8Params a) {
                 s1 = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a1, qreg[kk], s1, 0, 0, 0, 0, 0, 0);
             }
 
-            // ---- causal / tail mask (only blocks that reach past the wave's first query)
+            // ---- causal / tail mask (only blocks that reach past the wave's first query):
+            // key kb0 + off(r) + 4hh is visible iff off(r) <= min(qabs, S-1) - kb0 - 4hh
             const int kb0 = j * KB;
             if (kb0 + KB - 1 > qw0) {
+                const int lim = min(qabs, S - 1) - kb0 - 4 * hh;
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
-                    const int key = kb0 + 8 * (r >> 2) + 4 * hh + (r & 3);
-                    if (key > qabs || key >= S) s0[r] = -INFINITY;
-                    if (key + 32 > qabs || key + 32 >= S) s1[r] = -INFINITY;
+                    const int off = 8 * (r >> 2) + (r & 3);
+                    s0[r] = off <= lim ? s0[r] : -INFINITY;
+                    s1[r] = off + 32 <= lim ? s1[r] : -INFINITY;
                 }
             }
 
@@ -340,7 +342,7 @@ hipError_t launch_t(const Problem& p) {
 }  // namespace
 
 hipError_t launch_fp8(const Problem& p) {
-    constexpr int NW = 4;
+    constexpr int NW = 8;
     if (p.d_qk == 128) return p.p_mode == 0 ? launch_t<128, NW, 0>(p) : launch_t<128, NW, 1>(p);
     if (p.d_qk == 192) return p.p_mode == 0 ? launch_t<192, NW, 0>(p) : launch_t<192, NW, 1>(p);
     return hipErrorInvalidValue;
