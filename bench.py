@@ -10,7 +10,6 @@ when timing starts).  Throughput uses the causal FLOP count
 import argparse
 import json
 import os
-import subprocess
 import sys
 import time
 
@@ -38,25 +37,26 @@ def parse():
     ap.add_argument("--no-both-modes", dest="both_modes", action="store_false")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--calibrate-copy-mib", type=int, default=0,
+                    help="after timing, run one device-to-device copy of this many MiB "
+                         "(a known-size kernel for scaling HBM byte counters)")
     return ap.parse_args()
 
 
 def sclk_mhz():
-    """Current shader clock from amd-smi (None if unavailable)."""
-    try:
-        r = subprocess.run(["amd-smi", "metric", "-g", "0", "--clock", "--json"], capture_output=True,
-                           text=True, timeout=20)
-        data = json.loads(r.stdout)
-        if isinstance(data, list):
-            data = data[0]
-        clk = data.get("clock", data)
-        gfx = clk.get("gfx_0") or clk.get("GFX_0") or {}
-        v = gfx.get("clk")
-        if isinstance(v, dict):
-            v = v.get("value")
-        return float(v) if v is not None else None
-    except Exception:
-        return None
+    """Current shader clock (MHz) from the amdgpu sysfs DPM table, None if unavailable.
+
+    Read from a file: no helper program is started after the GPU is initialised."""
+    import glob
+    for path in sorted(glob.glob("/sys/class/drm/card*/device/pp_dpm_sclk")):
+        try:
+            for ln in open(path):
+                if ln.rstrip().endswith("*"):
+                    v = ln.split(":", 1)[1].strip().rstrip("*").strip().lower()
+                    return float(v.replace("mhz", ""))
+        except Exception:
+            continue
+    return None
 
 
 def time_launches(fn, steps, warmup, stream):
@@ -188,6 +188,14 @@ def main():
             "frac_of_peak": flops / (avg_ms * 1e-3) / 1e12 / peak,
         }
     clk_after = sclk_mhz()
+    if args.calibrate_copy_mib:
+        n = args.calibrate_copy_mib << 20
+        src = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     head = paths[modes[0]]
     value = head["tflops"]
     achieved = flops / (head["kernel_ms_avg"] * 1e-3) / 1e12

@@ -103,14 +103,18 @@ __global__ void __launch_bounds__(NW * 64) bf16_causal_fwd(Bf16Params a) {
 
     i32x4 kst[KPT];
     i32x4 vst[VPT];
+    // Stage loads of key block j; only a block that crosses S is predicated.
     auto gload = [&](int j) {
+        const bool full = (j + 1) * KB <= S;
 #pragma unroll
         for (int i = 0; i < KPT; ++i) {
             const int idx = tid + i * NT;
             if (T::K_CHUNKS % NT == 0 || idx < T::K_CHUNKS) {
                 const int row = idx / KCH_ROW, cc = idx % KCH_ROW;
                 const int key = j * KB + row;
-                kst[i] = key < S ? load16(kbase + (int64_t)key * k_row * 2 + 16 * cc) : i32x4{0, 0, 0, 0};
+                const uint8_t* src = kbase + (int64_t)key * k_row * 2 + 16 * cc;
+                if (full) kst[i] = load16(src);
+                else kst[i] = key < S ? load16(src) : i32x4{0, 0, 0, 0};
             }
         }
 #pragma unroll
@@ -119,7 +123,9 @@ __global__ void __launch_bounds__(NW * 64) bf16_causal_fwd(Bf16Params a) {
             if (T::V_CHUNKS % NT == 0 || idx < T::V_CHUNKS) {
                 const int row = idx >> 4, cc = idx & 15;
                 const int key = j * KB + row;
-                vst[i] = key < S ? load16(vbase + (int64_t)key * v_row * 2 + 16 * cc) : i32x4{0, 0, 0, 0};
+                const uint8_t* src = vbase + (int64_t)key * v_row * 2 + 16 * cc;
+                if (full) vst[i] = load16(src);
+                else vst[i] = key < S ? load16(src) : i32x4{0, 0, 0, 0};
             }
         }
     };
@@ -179,19 +185,21 @@ __global__ void __launch_bounds__(NW * 64) bf16_causal_fwd(Bf16Params a) {
                 s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, qreg[ks], s1, 0, 0, 0);
             }
 
+            // causal / tail mask: key kb0 + off(r) + 4hh is visible iff off(r) <= min(qabs, S-1) - kb0 - 4hh
             const int kb0 = j * KB;
             if (kb0 + KB - 1 > qw0) {
+                const int lim = min(qabs, S - 1) - kb0 - 4 * hh;
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
-                    const int key = kb0 + 8 * (r >> 2) + 4 * hh + (r & 3);
-                    if (key > qabs || key >= S) s0[r] = -INFINITY;
-                    if (key + 32 > qabs || key + 32 >= S) s1[r] = -INFINITY;
+                    const int off = 8 * (r >> 2) + (r & 3);
+                    s0[r] = off <= lim ? s0[r] : -INFINITY;
+                    s1[r] = off + 32 <= lim ? s1[r] : -INFINITY;
                 }
             }
 
             float mx = -INFINITY;
 #pragma unroll
-            for (int r = 0; r < 16; ++r) mx = fmaxf(mx, fmaxf(s0[r], s1[r]));
+            for (int r = 0; r < 16; ++r) mx = fmaxf(fmaxf(mx, s0[r]), s1[r]);
             mx = fmaxf(mx, other_half(mx));
             const float M = fmaxf(ceilf(mx * a.c), -1.0e30f);
             const bool need = M > ref + kRefSlack;

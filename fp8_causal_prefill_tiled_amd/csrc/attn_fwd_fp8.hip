@@ -62,21 +62,36 @@ struct Fp8Params {
 // distinct chunk positions, so the group's 128 bytes hit distinct banks.
 __device__ __forceinline__ int v_swz(int row) { return (row & 3) | (((row >> 3) & 1) << 2); }
 
-template <int DQK, int NW, int PMODE>
-__global__ void __launch_bounds__(NW * 64) fp8_causal_fwd(Fp8Params a) {
+// Two-wave ping-pong (wave specialisation) over a 3-stage LDS ring.
+//
+// The 8 waves form two groups, waves 0-3 and 4-7; the hardware places wave w and
+// wave w+4 on the same SIMD, so every SIMD holds one wave of each group.  Each
+// key block j is processed in two barrier-separated phases: while one group
+// issues matrix work (P.V of block j-1, then S^T of block j) the other group
+// computes block j-1's probabilities on the vector unit, and in the next phase
+// they swap ("Two-wave ping-pong schedule", Zyphra ZYFA page, MarkTechPost).  The
+// matrix phase raises its wave priority so its MFMAs issue as soon as the matrix
+// pipe frees.  Because group 1 lags group 0 by one phase, a K/V tile stays live
+// for two blocks: tile j+1 is written to ring slot (j+1)%3 at the start of
+// iteration j (the slot of tile j-2, whose last reader finished one phase
+// earlier) and its global loads were issued one iteration before that.
+template <int DQK, int PMODE>
+__global__ void __launch_bounds__(512, 2) fp8_causal_fwd(Fp8Params a) {
     using T = Fp8Tile<DQK>;
+    constexpr int NW = 8;
     constexpr int NT = NW * 64;
     constexpr int BM = NW * 32;
     constexpr int KPT = (T::K_CHUNKS + NT - 1) / NT;
     constexpr int VPT = (T::V_CHUNKS + NT - 1) / NT;
     constexpr int KCH_ROW = DQK / 16;
 
-    __shared__ __attribute__((aligned(16))) uint8_t smem_raw[2 * T::STAGE];
+    __shared__ __attribute__((aligned(16))) uint8_t smem_raw[3 * T::STAGE];
     ATTN_LDS uint8_t* smem = (ATTN_LDS uint8_t*)smem_raw;
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int w = tid >> 6;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave index, uniform
+    const int grp = w >> 2;                                    // ping-pong group
     const int BH = a.B * a.Hq;
     const int L = blockIdx.x;
     const int tile = a.n_tiles - 1 - L / BH;      // heaviest (longest causal prefix) tiles first
@@ -89,7 +104,6 @@ __global__ void __launch_bounds__(NW * 64) fp8_causal_fwd(Fp8Params a) {
     const int qw0 = q0 + 32 * w;
     const int kend = min(S, q0 + BM);
     const int nblk = (kend + KB - 1) / KB;                         // key blocks the workgroup stages
-    const int wnblk = qw0 < S ? (min(qw0 + 31, S - 1) / KB + 1) : 0;  // key blocks this wave uses
 
     const int c = lane & 31;
     const int hh = lane >> 5;
@@ -114,16 +128,21 @@ __global__ void __launch_bounds__(NW * 64) fp8_causal_fwd(Fp8Params a) {
         }
     }
 
+    // ---- K/V staging: global -> registers (gload) one iteration ahead, registers -> LDS ring (lstore).
+    // Only a block that crosses S needs per-lane predication (missing rows are zero-filled).
     i32x4 kst[KPT];
     i32x4 vst[VPT];
     auto gload = [&](int j) {
+        const bool full = (j + 1) * KB <= S;
 #pragma unroll
         for (int i = 0; i < KPT; ++i) {
             const int idx = tid + i * NT;
             if (T::K_CHUNKS % NT == 0 || idx < T::K_CHUNKS) {
                 const int row = idx / KCH_ROW, cc = idx % KCH_ROW;
                 const int key = j * KB + row;
-                kst[i] = key < S ? load16(kbase + key * k_row + 16 * cc) : i32x4{0, 0, 0, 0};
+                const uint8_t* src = kbase + (int64_t)key * k_row + 16 * cc;
+                if (full) kst[i] = load16(src);
+                else kst[i] = key < S ? load16(src) : i32x4{0, 0, 0, 0};
             }
         }
 #pragma unroll
@@ -132,12 +151,14 @@ __global__ void __launch_bounds__(NW * 64) fp8_causal_fwd(Fp8Params a) {
             if (T::V_CHUNKS % NT == 0 || idx < T::V_CHUNKS) {
                 const int row = idx >> 3, cc = idx & 7;
                 const int key = j * KB + row;
-                vst[i] = key < S ? load16(vbase + key * v_row + 16 * cc) : i32x4{0, 0, 0, 0};
+                const uint8_t* src = vbase + (int64_t)key * v_row + 16 * cc;
+                if (full) vst[i] = load16(src);
+                else vst[i] = key < S ? load16(src) : i32x4{0, 0, 0, 0};
             }
         }
     };
-    auto lstore = [&](int st) {
-        ATTN_LDS uint8_t* Ks = smem + st * T::STAGE;
+    auto lstore = [&](int j) {
+        ATTN_LDS uint8_t* Ks = smem + (j % 3) * T::STAGE;
         ATTN_LDS uint8_t* Vs = Ks + T::K_BYTES;
 #pragma unroll
         for (int i = 0; i < KPT; ++i) {
@@ -159,7 +180,10 @@ __global__ void __launch_bounds__(NW * 64) fp8_causal_fwd(Fp8Params a) {
 
     // Per-lane offsets of the transposing V reads: group G = lane/16 reads rows
     // (keys) of chunk cc in the order of the probability bytes, columns
-    // 32dt + 16(G&1) + [0,16).
+    // 32dt + 16(G&1) + [0,16).  The chunk of d-tile dt is 2dt + (G&1); since 2dt
+    // and G&1 share no bits, 16*((2dt + (G&1)) ^ s) == (32*dt) ^ (16*((G&1) ^ s)),
+    // so the tile offset is applied as voff ^ (32*dt) (bits 5-6, disjoint from
+    // key*128 and 8*(i&1)).
     int voff[4];
     {
         const int G = lane >> 4, i = lane & 15, k = i >> 1;
@@ -169,136 +193,211 @@ __global__ void __launch_bounds__(NW * 64) fp8_causal_fwd(Fp8Params a) {
             voff[cc] = key * 128 + 8 * (i & 1) + 16 * ((G & 1) ^ v_swz(key));
         }
     }
-    // The chunk of d-tile dt is 2dt + (G&1); since 2dt and G&1 share no bits,
-    // 16*((2dt + (G&1)) ^ s) == (32*dt) ^ (16*((G&1) ^ s)), so the tile offset is
-    // applied below as voff ^ (32*dt) (bits 5-6, disjoint from key*128 and 8*(i&1)).
 
     f32x16 o[4];
 #pragma unroll
     for (int dt = 0; dt < 4; ++dt) o[dt] = f32x16{0};
     f32x16 lacc = f32x16{0};
     float ref = -INFINITY;
-    const i32x8 ones = i32x8{0x38383838, 0x38383838, 0x38383838, 0x38383838,
-                             0x38383838, 0x38383838, 0x38383838, 0x38383838};
+    f32x16 s0, s1;          // S^T of the block between its matrix and its vector phase
+    i32x8 pv;               // e4m3 probabilities between the vector and the next matrix phase
+    int scale_b = 127;      // their E8M0 scale
+    // e4m3 1.0 in every byte: the A operand of the row-sum MFMA.  Kept live in
+    // VGPRs (the empty asm hides the constant, so it is not rebuilt per block).
+    i32x8 ones;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        int one4 = 0x38383838;
+        asm volatile("" : "+v"(one4));
+        ones[i] = one4;
+    }
 
+    // ---- matrix phase work.  Operands are double-buffered: the LDS reads for the
+    // next MFMA are issued before the current one, so LDS latency hides behind the
+    // 64-cycle matrix instructions instead of stalling each of them.
+    auto read_v = [&](const ATTN_LDS uint8_t* Vs, int dt) {
+        i32x8 va;
+#pragma unroll
+        for (int cc = 0; cc < 4; ++cc) {
+            i32x2 t = lds_read_tr8(Vs + (voff[cc] ^ (32 * dt)));
+            va[2 * cc] = t[0];
+            va[2 * cc + 1] = t[1];
+        }
+        return va;
+    };
+    auto read_k = [&](const ATTN_LDS uint8_t* Ks, int half, int kk) {
+        const ATTN_LDS uint8_t* kp = Ks + (c + 32 * half) * T::K_STRIDE + 64 * kk + 32 * hh;
+        i32x4 lo = lds_load16(kp), hi = lds_load16(kp + 16);
+        return i32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    };
+    // S^T = K . Q^T for keys [0,32) (s0) and [32,64) (s1) of block j
+    auto qk = [&](int j) {
+        const ATTN_LDS uint8_t* Ks = smem + (j % 3) * T::STAGE;
+        i32x8 k0 = read_k(Ks, 0, 0), k1 = read_k(Ks, 1, 0);
+        s0 = f32x16{0};
+        s1 = f32x16{0};
+#pragma unroll
+        for (int kk = 0; kk < T::NKK; ++kk) {
+            s0 = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(k0, qreg[kk], s0, 0, 0, 0, 0, 0, 0);
+            if (kk + 1 < T::NKK) k0 = read_k(Ks, 0, kk + 1);
+            s1 = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(k1, qreg[kk], s1, 0, 0, 0, 0, 0, 0);
+            if (kk + 1 < T::NKK) k1 = read_k(Ks, 1, kk + 1);
+        }
+    };
+    // O^T += V^T . P^T (scaled) and L += 1 . P^T (scaled) for block j
+    auto pvmma = [&](int j) {
+        const ATTN_LDS uint8_t* Vs = smem + (j % 3) * T::STAGE + T::K_BYTES;
+        i32x8 va0 = read_v(Vs, 0), va1 = read_v(Vs, 1);
+        o[0] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(va0, pv, o[0], 0, 0, 0, 127, 0, scale_b);
+        va0 = read_v(Vs, 2);
+        o[1] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(va1, pv, o[1], 0, 0, 0, 127, 0, scale_b);
+        va1 = read_v(Vs, 3);
+        o[2] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(va0, pv, o[2], 0, 0, 0, 127, 0, scale_b);
+        o[3] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(va1, pv, o[3], 0, 0, 0, 127, 0, scale_b);
+        lacc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(ones, pv, lacc, 0, 0, 0, 127, 0, scale_b);
+    };
+    // ---- probabilities of block j (vector unit): mask, block exponent, lazy reference, P bytes
+    auto softmax = [&](int j) {
+        // causal / tail mask, only on blocks that reach past the wave's first query:
+        // key kb0 + off(r) + 4hh is visible iff off(r) <= min(qabs, S-1) - kb0 - 4hh
+        const int kb0 = j * KB;
+        if (kb0 + KB - 1 > qw0) {
+            const int lim = min(qabs, S - 1) - kb0 - 4 * hh;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int off = 8 * (r >> 2) + (r & 3);
+                s0[r] = off <= lim ? s0[r] : -INFINITY;
+                s1[r] = off + 32 <= lim ? s1[r] : -INFINITY;
+            }
+        }
+        // block exponent M = ceil(max t)
+        float mx = -INFINITY;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) mx = fmaxf(fmaxf(mx, s0[r]), s1[r]);
+        mx = fmaxf(mx, other_half(mx));
+        const float M = fmaxf(ceilf(mx * a.c), -1.0e30f);  // floor: rows with no visible key here
+        // lazy power-of-two reference
+        const bool need = M > ref + kRefSlack;
+        if (__ballot(need)) {
+            const float nref = need ? M : ref;
+            const float f = need ? __builtin_amdgcn_exp2f(ref - nref) : 1.0f;
+#pragma unroll
+            for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) o[dt][r] *= f;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) lacc[r] *= f;
+            ref = nref;
+        }
+        scale_b = (int)fminf(fmaxf(M - 8.0f - ref, -127.0f), 127.0f) + 127;
+        int pw[8];
+        if (PMODE == 0) {
+            const float bias = 8.0f - M;
+#pragma unroll
+            for (int q4 = 0; q4 < 4; ++q4) {
+                float p0 = __builtin_amdgcn_exp2f(fmaf(s0[4 * q4 + 0], a.c, bias));
+                float p1 = __builtin_amdgcn_exp2f(fmaf(s0[4 * q4 + 1], a.c, bias));
+                float p2 = __builtin_amdgcn_exp2f(fmaf(s0[4 * q4 + 2], a.c, bias));
+                float p3 = __builtin_amdgcn_exp2f(fmaf(s0[4 * q4 + 3], a.c, bias));
+                int wd = __builtin_amdgcn_cvt_pk_fp8_f32(p0, p1, 0, false);
+                pw[q4] = __builtin_amdgcn_cvt_pk_fp8_f32(p2, p3, wd, true);
+                p0 = __builtin_amdgcn_exp2f(fmaf(s1[4 * q4 + 0], a.c, bias));
+                p1 = __builtin_amdgcn_exp2f(fmaf(s1[4 * q4 + 1], a.c, bias));
+                p2 = __builtin_amdgcn_exp2f(fmaf(s1[4 * q4 + 2], a.c, bias));
+                p3 = __builtin_amdgcn_exp2f(fmaf(s1[4 * q4 + 3], a.c, bias));
+                wd = __builtin_amdgcn_cvt_pk_fp8_f32(p0, p1, 0, false);
+                pw[4 + q4] = __builtin_amdgcn_cvt_pk_fp8_f32(p2, p3, wd, true);
+            }
+        } else {
+            const float bc = 120.0f - 8.0f * M;
+#pragma unroll
+            for (int q4 = 0; q4 < 4; ++q4) {
+                unsigned wd = 0;
+                wd = __builtin_amdgcn_cvt_pk_u8_f32(fmaf(s0[4 * q4 + 0], a.a8, bc), 0, wd);
+                wd = __builtin_amdgcn_cvt_pk_u8_f32(fmaf(s0[4 * q4 + 1], a.a8, bc), 1, wd);
+                wd = __builtin_amdgcn_cvt_pk_u8_f32(fmaf(s0[4 * q4 + 2], a.a8, bc), 2, wd);
+                wd = __builtin_amdgcn_cvt_pk_u8_f32(fmaf(s0[4 * q4 + 3], a.a8, bc), 3, wd);
+                pw[q4] = (int)wd;
+                wd = 0;
+                wd = __builtin_amdgcn_cvt_pk_u8_f32(fmaf(s1[4 * q4 + 0], a.a8, bc), 0, wd);
+                wd = __builtin_amdgcn_cvt_pk_u8_f32(fmaf(s1[4 * q4 + 1], a.a8, bc), 1, wd);
+                wd = __builtin_amdgcn_cvt_pk_u8_f32(fmaf(s1[4 * q4 + 2], a.a8, bc), 2, wd);
+                wd = __builtin_amdgcn_cvt_pk_u8_f32(fmaf(s1[4 * q4 + 3], a.a8, bc), 3, wd);
+                pw[4 + q4] = (int)wd;
+            }
+        }
+        pv = i32x8{pw[0], pw[1], pw[2], pw[3], pw[4], pw[5], pw[6], pw[7]};
+    };
+
+    // ---- schedule.  Every wave walks all nblk staged blocks: a block wholly above
+    // a wave's queries is fully masked, gives p = 0 and adds exactly nothing, and
+    // keeping the work uniform leaves each group's loop one straight path (the few
+    // extra diagonal MFMAs would otherwise be idle barrier time).  The two groups
+    // run separate loops with the same number of barriers:
+    //   iteration j, phase A: group 0 P.V(j-1) + S^T(j)   group 1 softmax(j-1)
+    //                phase B: group 0 softmax(j)          group 1 P.V(j-1) + S^T(j)
+    // All waves stage tile j+1 into the ring and issue the loads of tile j+2 at
+    // the start of phase A.
+    // A phase boundary: a workgroup barrier that the compiler may not schedule
+    // any instruction across, so each phase's work stays inside its phase.
+    auto phase_barrier = [&]() {
+        __builtin_amdgcn_sched_barrier(0);
+        __syncthreads();
+        __builtin_amdgcn_sched_barrier(0);
+    };
+    auto stage = [&](int j) {
+        if (j + 1 < nblk) lstore(j + 1);
+        if (j + 2 < nblk) gload(j + 2);
+    };
     gload(0);
     lstore(0);
-    __syncthreads();
+    if (nblk > 1) gload(1);
+    phase_barrier();
 
-    for (int j = 0; j < nblk; ++j) {
-        const int st = j & 1;
-        if (j + 1 < nblk) gload(j + 1);
-        if (j < wnblk) {
-            const ATTN_LDS uint8_t* Ks = smem + st * T::STAGE;
-            const ATTN_LDS uint8_t* Vs = Ks + T::K_BYTES;
-
-            // ---- S^T = K . Q^T for keys [0,32) and [32,64) of the block
-            f32x16 s0 = f32x16{0}, s1 = f32x16{0};
-#pragma unroll
-            for (int kk = 0; kk < T::NKK; ++kk) {
-                const ATTN_LDS uint8_t* kp = Ks + c * T::K_STRIDE + 64 * kk + 32 * hh;
-                i32x4 a0l = lds_load16(kp), a0h = lds_load16(kp + 16);
-                i32x4 a1l = lds_load16(kp + 32 * T::K_STRIDE), a1h = lds_load16(kp + 32 * T::K_STRIDE + 16);
-                i32x8 a0 = i32x8{a0l[0], a0l[1], a0l[2], a0l[3], a0h[0], a0h[1], a0h[2], a0h[3]};
-                i32x8 a1 = i32x8{a1l[0], a1l[1], a1l[2], a1l[3], a1h[0], a1h[1], a1h[2], a1h[3]};
-                s0 = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a0, qreg[kk], s0, 0, 0, 0, 0, 0, 0);
-                s1 = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a1, qreg[kk], s1, 0, 0, 0, 0, 0, 0);
-            }
-
-            // ---- causal / tail mask (only blocks that reach past the wave's first query):
-            // key kb0 + off(r) + 4hh is visible iff off(r) <= min(qabs, S-1) - kb0 - 4hh
-            const int kb0 = j * KB;
-            if (kb0 + KB - 1 > qw0) {
-                const int lim = min(qabs, S - 1) - kb0 - 4 * hh;
-#pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int off = 8 * (r >> 2) + (r & 3);
-                    s0[r] = off <= lim ? s0[r] : -INFINITY;
-                    s1[r] = off + 32 <= lim ? s1[r] : -INFINITY;
-                }
-            }
-
-            // ---- block exponent M = ceil(max t)
-            float mx = -INFINITY;
-#pragma unroll
-            for (int r = 0; r < 16; ++r) mx = fmaxf(mx, fmaxf(s0[r], s1[r]));
-            mx = fmaxf(mx, other_half(mx));
-            const float M = fmaxf(ceilf(mx * a.c), -1.0e30f);  // floor: rows with no visible key here
-
-            // ---- lazy power-of-two reference
-            const bool need = M > ref + kRefSlack;
-            if (__ballot(need)) {
-                const float nref = need ? M : ref;
-                const float f = need ? __builtin_amdgcn_exp2f(ref - nref) : 1.0f;
-#pragma unroll
-                for (int dt = 0; dt < 4; ++dt)
-#pragma unroll
-                    for (int r = 0; r < 16; ++r) o[dt][r] *= f;
-#pragma unroll
-                for (int r = 0; r < 16; ++r) lacc[r] *= f;
-                ref = nref;
-            }
-            const int scale_b = (int)fminf(fmaxf(M - 8.0f - ref, -127.0f), 127.0f) + 127;
-
-            // ---- probabilities as e4m3 bytes, in B-operand order
-            int pw[8];
-            if (PMODE == 0) {
-                const float bias = 8.0f - M;
-#pragma unroll
-                for (int q4 = 0; q4 < 4; ++q4) {
-                    float p0 = __builtin_amdgcn_exp2f(fmaf(s0[4 * q4 + 0], a.c, bias));
-                    float p1 = __builtin_amdgcn_exp2f(fmaf(s0[4 * q4 + 1], a.c, bias));
-                    float p2 = __builtin_amdgcn_exp2f(fmaf(s0[4 * q4 + 2], a.c, bias));
-                    float p3 = __builtin_amdgcn_exp2f(fmaf(s0[4 * q4 + 3], a.c, bias));
-                    int wd = __builtin_amdgcn_cvt_pk_fp8_f32(p0, p1, 0, false);
-                    pw[q4] = __builtin_amdgcn_cvt_pk_fp8_f32(p2, p3, wd, true);
-                    p0 = __builtin_amdgcn_exp2f(fmaf(s1[4 * q4 + 0], a.c, bias));
-                    p1 = __builtin_amdgcn_exp2f(fmaf(s1[4 * q4 + 1], a.c, bias));
-                    p2 = __builtin_amdgcn_exp2f(fmaf(s1[4 * q4 + 2], a.c, bias));
-                    p3 = __builtin_amdgcn_exp2f(fmaf(s1[4 * q4 + 3], a.c, bias));
-                    wd = __builtin_amdgcn_cvt_pk_fp8_f32(p0, p1, 0, false);
-                    pw[4 + q4] = __builtin_amdgcn_cvt_pk_fp8_f32(p2, p3, wd, true);
-                }
-            } else {
-                const float bc = 120.0f - 8.0f * M;
-#pragma unroll
-                for (int q4 = 0; q4 < 4; ++q4) {
-                    unsigned wd = 0;
-                    wd = __builtin_amdgcn_cvt_pk_u8_f32(fmaf(s0[4 * q4 + 0], a.a8, bc), 0, wd);
-                    wd = __builtin_amdgcn_cvt_pk_u8_f32(fmaf(s0[4 * q4 + 1], a.a8, bc), 1, wd);
-                    wd = __builtin_amdgcn_cvt_pk_u8_f32(fmaf(s0[4 * q4 + 2], a.a8, bc), 2, wd);
-                    wd = __builtin_amdgcn_cvt_pk_u8_f32(fmaf(s0[4 * q4 + 3], a.a8, bc), 3, wd);
-                    pw[q4] = (int)wd;
-                    wd = 0;
-                    wd = __builtin_amdgcn_cvt_pk_u8_f32(fmaf(s1[4 * q4 + 0], a.a8, bc), 0, wd);
-                    wd = __builtin_amdgcn_cvt_pk_u8_f32(fmaf(s1[4 * q4 + 1], a.a8, bc), 1, wd);
-                    wd = __builtin_amdgcn_cvt_pk_u8_f32(fmaf(s1[4 * q4 + 2], a.a8, bc), 2, wd);
-                    wd = __builtin_amdgcn_cvt_pk_u8_f32(fmaf(s1[4 * q4 + 3], a.a8, bc), 3, wd);
-                    pw[4 + q4] = (int)wd;
-                }
-            }
-            const i32x8 pv = i32x8{pw[0], pw[1], pw[2], pw[3], pw[4], pw[5], pw[6], pw[7]};
-
-            // ---- O^T += V^T . P^T (scaled), L += 1 . P^T (scaled)
-#pragma unroll
-            for (int dt = 0; dt < 4; ++dt) {
-                i32x8 va;
-#pragma unroll
-                for (int cc = 0; cc < 4; ++cc) {
-                    i32x2 t = lds_read_tr8(Vs + (voff[cc] ^ (32 * dt)));
-                    va[2 * cc] = t[0];
-                    va[2 * cc + 1] = t[1];
-                }
-                o[dt] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(va, pv, o[dt], 0, 0, 0, 127, 0, scale_b);
-            }
-            lacc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(ones, pv, lacc, 0, 0, 0, 127, 0, scale_b);
+    if (grp == 0) {
+        stage(0);
+        __builtin_amdgcn_s_setprio(1);
+        qk(0);
+        __builtin_amdgcn_s_setprio(0);
+        phase_barrier();
+        softmax(0);
+        phase_barrier();
+        for (int j = 1; j < nblk; ++j) {
+            stage(j);
+            __builtin_amdgcn_s_setprio(1);
+            pvmma(j - 1);
+            qk(j);
+            __builtin_amdgcn_s_setprio(0);
+            phase_barrier();
+            softmax(j);
+            phase_barrier();
         }
-        if (j + 1 < nblk) lstore(st ^ 1);
-        __syncthreads();
+        pvmma(nblk - 1);
+        phase_barrier();
+    } else {
+        stage(0);
+        phase_barrier();
+        __builtin_amdgcn_s_setprio(1);
+        qk(0);
+        __builtin_amdgcn_s_setprio(0);
+        phase_barrier();
+        for (int j = 1; j < nblk; ++j) {
+            stage(j);
+            softmax(j - 1);
+            phase_barrier();
+            __builtin_amdgcn_s_setprio(1);
+            pvmma(j - 1);
+            qk(j);
+            __builtin_amdgcn_s_setprio(0);
+            phase_barrier();
+        }
+        softmax(nblk - 1);
+        phase_barrier();
+        pvmma(nblk - 1);
     }
 
     // ---- epilogue: out = bf16(v_scale * (O / L)), lane holds query c, d = 32dt + 8(r/4) + 4hh + r%4
-    if (qabs < S && wnblk > 0) {
+    if (qabs < S) {
         const float lsum = lacc[0];
         __bf16* op = a.o + (((int64_t)b * S + qabs) * a.Hq + h) * 128;
 #pragma unroll
@@ -316,8 +415,9 @@ __global__ void __launch_bounds__(NW * 64) fp8_causal_fwd(Fp8Params a) {
     }
 }
 
-template <int DQK, int NW, int PMODE>
+template <int DQK, int PMODE>
 hipError_t launch_t(const Problem& p) {
+    constexpr int NW = 8;
     constexpr int BM = NW * 32;
     Fp8Params a;
     a.q = static_cast<const uint8_t*>(p.q);
@@ -335,16 +435,15 @@ hipError_t launch_t(const Problem& p) {
     a.n_tiles = (p.S + BM - 1) / BM;
     const long long nblocks = (long long)a.n_tiles * p.B * p.Hq;
     if (nblocks <= 0 || nblocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-    hipLaunchKernelGGL((fp8_causal_fwd<DQK, NW, PMODE>), dim3((unsigned)nblocks), dim3(NW * 64), 0, p.stream, a);
+    hipLaunchKernelGGL((fp8_causal_fwd<DQK, PMODE>), dim3((unsigned)nblocks), dim3(NW * 64), 0, p.stream, a);
     return hipGetLastError();
 }
 
 }  // namespace
 
 hipError_t launch_fp8(const Problem& p) {
-    constexpr int NW = 8;
-    if (p.d_qk == 128) return p.p_mode == 0 ? launch_t<128, NW, 0>(p) : launch_t<128, NW, 1>(p);
-    if (p.d_qk == 192) return p.p_mode == 0 ? launch_t<192, NW, 0>(p) : launch_t<192, NW, 1>(p);
+    if (p.d_qk == 128) return p.p_mode == 0 ? launch_t<128, 0>(p) : launch_t<128, 1>(p);
+    if (p.d_qk == 192) return p.p_mode == 0 ? launch_t<192, 0>(p) : launch_t<192, 1>(p);
     return hipErrorInvalidValue;
 }
 
