@@ -59,6 +59,23 @@ def sclk_mhz():
     return None
 
 
+def measured_traffic(workload, mode):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, or None when the
+    kernel source has changed since those counters were taken (or no summary exists)."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    try:
+        t = json.load(open(path))
+        src = open(os.path.join(ROOT, t["source"]), "rb").read()
+    except Exception:
+        return None
+    if hashlib.sha256(src).hexdigest()[:16] != t["source_sha256_16"]:
+        return None
+    if t["workload"] != workload or t["p_mode"] != mode:
+        return None
+    return t["hbm_read_bytes_per_launch"] + t["hbm_write_bytes_per_launch"]
+
+
 def time_launches(fn, steps, warmup, stream):
     import torch
     for _ in range(warmup):
@@ -79,48 +96,48 @@ def time_launches(fn, steps, warmup, stream):
 
 def cpu_baseline(w, d, out_gpu, seconds, dtype):
     """Time the CPU oracle (fp64 attention) on a bounded sample of the same workload and
-    compare the GPU output on those rows.  Returns the cpu_baseline object."""
+    compare the GPU output on those rows.  Returns the cpu_baseline object.
+
+    Sample: query rows spread over 0..S-1 (longest causal prefixes first), in chunks of 64,
+    for three heads, until about `seconds` of oracle time has been spent."""
     import numpy as np
     from threadpoolctl import threadpool_info
-    from oracle.attention64 import attention_fp64, dequantize, rel_rms
+    from oracle.attention64 import attention_fp64, dequantize
 
     threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
     S = w.S
-    rows_per_chunk = 64
-    # rows spread over the sequence, longest prefixes first
-    order = np.linspace(S - 1, 0, 512).astype(np.int64)
+    order = np.linspace(S - 1, 0, 4096).astype(np.int64)
     heads = [0, w.Hq // 2, w.Hq - 1]
-    flops = 0.0
-    done_rows = []
+    per_head = []
+    for h in heads:
+        g = h // (w.Hq // w.Hkv)
+        if dtype == "fp8":
+            per_head.append((h, dequantize(d["q8"][:, :, h:h + 1].numpy(), d["q_scale"]),
+                             dequantize(d["k8"][:, :, g:g + 1].numpy(), d["k_scale"]),
+                             dequantize(d["v8"][:, :, g:g + 1].numpy(), d["v_scale"])))
+        else:
+            per_head.append((h, d["q"][:, :, h:h + 1].float().numpy(), d["k"][:, :, g:g + 1].float().numpy(),
+                             d["v"][:, :, g:g + 1].float().numpy()))
+    flops, el, nrows = 0.0, 0.0, 0
     errs_num, errs_den = 0.0, 0.0
-    t0 = time.perf_counter()
     i = 0
-    while time.perf_counter() - t0 < seconds and i < len(order):
-        rows = np.sort(order[i:i + rows_per_chunk])
-        i += rows_per_chunk
-        for h in heads:
-            g = h // (w.Hq // w.Hkv)
-            if dtype == "fp8":
-                q = dequantize(d["q8"][:, :, h:h + 1].numpy(), d["q_scale"])
-                k = dequantize(d["k8"][:, :, g:g + 1].numpy(), d["k_scale"])
-                v = dequantize(d["v8"][:, :, g:g + 1].numpy(), d["v_scale"])
-            else:
-                q = d["q"][:, :, h:h + 1].float().numpy()
-                k = d["k"][:, :, g:g + 1].float().numpy()
-                v = d["v"][:, :, g:g + 1].float().numpy()
-            ts = time.perf_counter()
+    while el < seconds and i < len(order):
+        rows = np.sort(order[i:i + 64])
+        i += 64
+        nrows += len(rows)
+        for h, q, k, v in per_head:
+            t0 = time.perf_counter()
             ref = attention_fp64(q, k, v, rows=rows)
+            el += time.perf_counter() - t0
             flops += float(np.sum(2.0 * (rows + 1) * (w.d_qk + w.d_v)))
             got = out_gpu[:, rows, h:h + 1].astype(np.float64)
             errs_num += float(np.sum((got - ref) ** 2))
             errs_den += float(np.sum(ref ** 2))
-            done_rows.append(len(rows))
-    el = time.perf_counter() - t0
     return {
         "value": flops / el / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
-        "sample": f"fp64 attention (oracle/attention64.py, numpy+BLAS) on {sum(done_rows)//len(heads)} query rows "
-                  f"(spread over 0..S-1, longest first) x heads {heads} of the {w.name} workload, "
-                  f"{el:.1f} s; FLOPs counted 2*(i+1)*(d_qk+d_v) per row",
+        "sample": f"fp64 attention (oracle/attention64.py, numpy+BLAS) on {nrows} query rows "
+                  f"(spread over 0..S-1, longest prefixes first) x heads {heads} of the {w.name} workload, "
+                  f"{el:.1f} s of oracle time; FLOPs counted 2*(i+1)*(d_qk+d_v) per row i",
         "gpu_rel_rms_vs_oracle_on_sample": float(np.sqrt(errs_num / errs_den)),
         "cpu_model": _cpu_model(),
         "os_cpu_count": os.cpu_count(),
@@ -225,7 +242,8 @@ def main():
                    "causal_tflop_per_step": flops / 1e12},
         "frac_of_peak": value / peak,
         "roofline": {"bound": "mfma", "achieved": achieved, "peak": peak, "unit": "TFLOP/s",
-                     "frac": achieved / peak, "traffic": None,
+                     "frac": achieved / peak,
+                     "traffic": measured_traffic(w.name, modes[0]) if args.dtype == "fp8" else None,
                      "kernel": f"{args.dtype}_causal_fwd", "per_launch_tflop": flops / 1e12},
         "paths": paths,
         "sclk_mhz": {"before": clk_before, "after": clk_after},
