@@ -39,8 +39,13 @@ struct Fp8Tile {
     static constexpr int NKK = DQK / 64;          // 32x32x64 steps over d_qk
     static constexpr int K_STRIDE = DQK + 16;     // padded LDS row of K, bytes
     static constexpr int K_BYTES = KB * K_STRIDE;
-    static constexpr int V_BYTES = KB * 128;      // d_v = 128 bytes per key, chunk-swizzled
-    static constexpr int STAGE = K_BYTES + V_BYTES;
+    static constexpr int V_BYTES = KB * 128;      // key-major V staging tile, chunk-swizzled
+    static constexpr int VT_STRIDE = KB + 16;     // padded LDS row of V^T (one d, 64 keys), bytes
+    static constexpr int VT_BYTES = 128 * VT_STRIDE;
+    // LDS: 3 K slots, 3 V^T slots, 2 key-major V staging tiles
+    static constexpr int OFF_VT = 3 * K_BYTES;
+    static constexpr int OFF_VS = OFF_VT + 3 * VT_BYTES;
+    static constexpr int LDS_BYTES = OFF_VS + 2 * V_BYTES;
     static constexpr int K_CHUNKS = KB * DQK / 16;
     static constexpr int V_CHUNKS = KB * 128 / 16;
 };
@@ -62,36 +67,47 @@ struct Fp8Params {
 // distinct chunk positions, so the group's 128 bytes hit distinct banks.
 __device__ __forceinline__ int v_swz(int row) { return (row & 3) | (((row >> 3) & 1) << 2); }
 
-// Two-wave ping-pong (wave specialisation) over a 3-stage LDS ring.
+// One wave per SIMD, two query halves in ping-pong.
 //
-// The 8 waves form two groups, waves 0-3 and 4-7; the hardware places wave w and
-// wave w+4 on the same SIMD, so every SIMD holds one wave of each group.  Each
-// key block j is processed in two barrier-separated phases: while one group
-// issues matrix work (P.V of block j-1, then S^T of block j) the other group
-// computes block j-1's probabilities on the vector unit, and in the next phase
-// they swap ("Two-wave ping-pong schedule", Zyphra ZYFA page, MarkTechPost).  The
-// matrix phase raises its wave priority so its MFMAs issue as soon as the matrix
-// pipe frees.  Because group 1 lags group 0 by one phase, a K/V tile stays live
-// for two blocks: tile j+1 is written to ring slot (j+1)%3 at the start of
-// iteration j (the slot of tile j-2, whose last reader finished one phase
-// earlier) and its global loads were issued one iteration before that.
+// A workgroup of 4 waves (one per SIMD, 512 registers each) covers 256 query
+// rows of one head; wave w owns rows [64w, 64w + 64) of the tile as two 32-row
+// halves A and B.  Each iteration j is two phases whose matrix and vector work
+// are independent of each other:
+//     phase 1:  MFMA  P.V of half B, block j-1  and  S^T of half B, block j
+//               VALU  probabilities of half A, block j
+//     phase 2:  MFMA  S^T of half A, block j+1  and  P.V of half A, block j
+//               VALU  probabilities of half B, block j
+// This is the pages' two-wave ping-pong ("Two-wave ping-pong schedule", Zyphra
+// ZYFA page, MarkTechPost) moved inside one wave: the two halves take the roles
+// of the two waves, and within a phase the scheduler interleaves each 64-cycle
+// 32x32x64 MFMA with the ~10 vector instructions that gfx950 issues in its
+// shadow from the same wave.  Only two score tiles are live at any time.
+//
+// LDS.  K tiles (row-major, padded rows) and V^T tiles each live in 3 slots; V^T
+// row d holds the block's 64 keys in the byte order of the probability operand,
+// so both matrix operands are plain 16-byte LDS reads.  V^T is built once per
+// workgroup from a key-major staging tile (2 slots) with the transposing
+// ds_read_b64_tr_b8, which is far slower per byte than ds_read_b128 on gfx950,
+// so it is paid once per tile rather than once per wave.  Iteration j builds
+// V^T(j+1), stores K(j+2) and V(j+2) from registers and issues the global loads
+// of tile j+3; one barrier ends the iteration.
 template <int DQK, int PMODE>
-__global__ void __launch_bounds__(512, 2) fp8_causal_fwd(Fp8Params a) {
+__global__ void __launch_bounds__(256, 1) fp8_causal_fwd(Fp8Params a) {
     using T = Fp8Tile<DQK>;
-    constexpr int NW = 8;
+    constexpr int NW = 4;
     constexpr int NT = NW * 64;
-    constexpr int BM = NW * 32;
+    constexpr int BM = NW * 64;
     constexpr int KPT = (T::K_CHUNKS + NT - 1) / NT;
     constexpr int VPT = (T::V_CHUNKS + NT - 1) / NT;
+    constexpr int TPT = (128 * 4) / NT;          // V^T chunks built per thread
     constexpr int KCH_ROW = DQK / 16;
 
-    __shared__ __attribute__((aligned(16))) uint8_t smem_raw[3 * T::STAGE];
+    __shared__ __attribute__((aligned(16))) uint8_t smem_raw[T::LDS_BYTES];
     ATTN_LDS uint8_t* smem = (ATTN_LDS uint8_t*)smem_raw;
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave index, uniform
-    const int grp = w >> 2;                                    // ping-pong group
     const int BH = a.B * a.Hq;
     const int L = blockIdx.x;
     const int tile = a.n_tiles - 1 - L / BH;      // heaviest (longest causal prefix) tiles first
@@ -101,13 +117,14 @@ __global__ void __launch_bounds__(512, 2) fp8_causal_fwd(Fp8Params a) {
     const int g = h / (a.Hq / a.Hkv);
     const int S = a.S;
     const int q0 = tile * BM;
-    const int qw0 = q0 + 32 * w;
+    const int qw0 = q0 + 64 * w;
     const int kend = min(S, q0 + BM);
-    const int nblk = (kend + KB - 1) / KB;                         // key blocks the workgroup stages
+    const int nblk = (kend + KB - 1) / KB;        // key blocks the workgroup walks
 
     const int c = lane & 31;
     const int hh = lane >> 5;
-    const int qabs = qw0 + c;
+    const int qA = qw0 + c;                       // query of this lane in half A
+    const int qB = qw0 + 32 + c;                  // and in half B
 
     const int64_t q_row = (int64_t)a.Hq * DQK;
     const int64_t k_row = (int64_t)a.Hkv * DQK;
@@ -115,34 +132,34 @@ __global__ void __launch_bounds__(512, 2) fp8_causal_fwd(Fp8Params a) {
     const uint8_t* kbase = a.k + (int64_t)b * S * k_row + (int64_t)g * DQK;
     const uint8_t* vbase = a.v + (int64_t)b * S * v_row + (int64_t)g * 128;
 
-    // Q^T operand: lane (query c, half hh) holds d in [64kk + 32hh, +32) for each step kk.
-    i32x8 qreg[T::NKK];
-    {
+    // Q^T operands: lane (query c, half hh) holds d in [64kk + 32hh, +32) for each step kk.
+    i32x8 qa[T::NKK], qb[T::NKK];
+    auto load_q = [&](int qabs, i32x8 (&qr)[T::NKK]) {
         const bool ok = qabs < S;
         const uint8_t* qp = a.q + ((int64_t)b * S + (ok ? qabs : 0)) * q_row + (int64_t)h * DQK + 32 * hh;
 #pragma unroll
         for (int kk = 0; kk < T::NKK; ++kk) {
             i32x4 lo = ok ? load16(qp + 64 * kk) : i32x4{0, 0, 0, 0};
             i32x4 hi = ok ? load16(qp + 64 * kk + 16) : i32x4{0, 0, 0, 0};
-            qreg[kk] = i32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+            qr[kk] = i32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
         }
-    }
+    };
+    load_q(qA, qa);
+    load_q(qB, qb);
 
-    // ---- K/V staging: global -> registers (gload) one iteration ahead, registers -> LDS ring (lstore).
-    // Only a block that crosses S needs per-lane predication (missing rows are zero-filled).
+    // ---- staging: global -> registers two iterations ahead (gload), registers -> LDS (lstore).
+    // Rows past S are clamped to row S-1: they are loaded in bounds, their scores are
+    // always masked and their probabilities are exactly zero, so the load is branch-free.
     i32x4 kst[KPT];
     i32x4 vst[VPT];
     auto gload = [&](int j) {
-        const bool full = (j + 1) * KB <= S;
 #pragma unroll
         for (int i = 0; i < KPT; ++i) {
             const int idx = tid + i * NT;
             if (T::K_CHUNKS % NT == 0 || idx < T::K_CHUNKS) {
                 const int row = idx / KCH_ROW, cc = idx % KCH_ROW;
-                const int key = j * KB + row;
-                const uint8_t* src = kbase + (int64_t)key * k_row + 16 * cc;
-                if (full) kst[i] = load16(src);
-                else kst[i] = key < S ? load16(src) : i32x4{0, 0, 0, 0};
+                const int key = min(j * KB + row, S - 1);
+                kst[i] = load16(kbase + (int64_t)key * k_row + 16 * cc);
             }
         }
 #pragma unroll
@@ -150,16 +167,14 @@ __global__ void __launch_bounds__(512, 2) fp8_causal_fwd(Fp8Params a) {
             const int idx = tid + i * NT;
             if (T::V_CHUNKS % NT == 0 || idx < T::V_CHUNKS) {
                 const int row = idx >> 3, cc = idx & 7;
-                const int key = j * KB + row;
-                const uint8_t* src = vbase + (int64_t)key * v_row + 16 * cc;
-                if (full) vst[i] = load16(src);
-                else vst[i] = key < S ? load16(src) : i32x4{0, 0, 0, 0};
+                const int key = min(j * KB + row, S - 1);
+                vst[i] = load16(vbase + (int64_t)key * v_row + 16 * cc);
             }
         }
     };
-    auto lstore = [&](int j) {
-        ATTN_LDS uint8_t* Ks = smem + (j % 3) * T::STAGE;
-        ATTN_LDS uint8_t* Vs = Ks + T::K_BYTES;
+    auto lstore = [&](int j) {   // K(j) -> K slot j%3, V(j) -> staging slot j%2
+        ATTN_LDS uint8_t* Ks = smem + (j % 3) * T::K_BYTES;
+        ATTN_LDS uint8_t* Vs = smem + T::OFF_VS + (j & 1) * T::V_BYTES;
 #pragma unroll
         for (int i = 0; i < KPT; ++i) {
             const int idx = tid + i * NT;
@@ -178,32 +193,55 @@ __global__ void __launch_bounds__(512, 2) fp8_causal_fwd(Fp8Params a) {
         }
     };
 
-    // Per-lane offsets of the transposing V reads: group G = lane/16 reads rows
-    // (keys) of chunk cc in the order of the probability bytes, columns
-    // 32dt + 16(G&1) + [0,16).  The chunk of d-tile dt is 2dt + (G&1); since 2dt
-    // and G&1 share no bits, 16*((2dt + (G&1)) ^ s) == (32*dt) ^ (16*((G&1) ^ s)),
-    // so the tile offset is applied as voff ^ (32*dt) (bits 5-6, disjoint from
-    // key*128 and 8*(i&1)).
-    int voff[4];
-    {
-        const int G = lane >> 4, i = lane & 15, k = i >> 1;
+    // ---- V^T construction: V^T row d holds the 64 keys at positions p = 32h + t in the
+    // probability-byte order key(h, t) = 32(t/16) + 8((t%16)/4) + 4h + t%4.  16-lane group
+    // G (of 32) builds the chunk d in [16(G%8), +16), p in [16(G/8), +16) from two
+    // transposing reads of 8 keys (rows) x 16 d (columns) of the key-major staging tile.
+    int tr_off[TPT][2];
+    int tr_dst[TPT];
 #pragma unroll
-        for (int cc = 0; cc < 4; ++cc) {
-            const int key = 32 * (cc >> 1) + 16 * (cc & 1) + 8 * (k >> 2) + 4 * hh + (k & 3);
-            voff[cc] = key * 128 + 8 * (i & 1) + 16 * ((G & 1) ^ v_swz(key));
+    for (int u = 0; u < TPT; ++u) {
+        const int G = 4 * w + (lane >> 4) + 16 * u, n = lane & 15, t = n >> 1;
+        const int dbase = 16 * (G & 7), p0 = 16 * (G >> 3);
+#pragma unroll
+        for (int x = 0; x < 2; ++x) {
+            const int pos = p0 + 8 * x + t;
+            const int hk = pos >> 5, tk = pos & 31;
+            const int key = 32 * (tk >> 4) + 8 * ((tk & 15) >> 2) + 4 * hk + (tk & 3);
+            tr_off[u][x] = key * 128 + 16 * ((dbase >> 4) ^ v_swz(key)) + 8 * (n & 1);
         }
+        tr_dst[u] = (dbase + n) * T::VT_STRIDE + p0;
     }
-
-    f32x16 o[4];
+    i32x2 tlo[TPT], thi[TPT];
+    auto transpose_read = [&](int j) {   // staging slot j%2 -> registers
+        const ATTN_LDS uint8_t* Vs = smem + T::OFF_VS + (j & 1) * T::V_BYTES;
 #pragma unroll
-    for (int dt = 0; dt < 4; ++dt) o[dt] = f32x16{0};
-    f32x16 lacc = f32x16{0};
-    float ref = -INFINITY;
-    f32x16 s0, s1;          // S^T of the block between its matrix and its vector phase
-    i32x8 pv;               // e4m3 probabilities between the vector and the next matrix phase
-    int scale_b = 127;      // their E8M0 scale
+        for (int u = 0; u < TPT; ++u) {
+            tlo[u] = lds_read_tr8(Vs + tr_off[u][0]);
+            thi[u] = lds_read_tr8(Vs + tr_off[u][1]);
+        }
+    };
+    auto transpose_write = [&](int j) {   // registers -> V^T slot j%3
+#pragma unroll
+        for (int u = 0; u < TPT; ++u)
+            lds_store16(smem + T::OFF_VT + (j % 3) * T::VT_BYTES + tr_dst[u],
+                        i32x4{tlo[u][0], tlo[u][1], thi[u][0], thi[u][1]});
+    };
+    auto transpose_v = [&](int j) {
+        transpose_read(j);
+        transpose_write(j);
+    };
+
+    f32x16 oa[4], ob[4];
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt) {
+        oa[dt] = f32x16{0};
+        ob[dt] = f32x16{0};
+    }
+    f32x16 la = f32x16{0}, lb = f32x16{0};
+    float refa = -INFINITY, refb = -INFINITY;
     // e4m3 1.0 in every byte: the A operand of the row-sum MFMA.  Kept live in
-    // VGPRs (the empty asm hides the constant, so it is not rebuilt per block).
+    // registers (the empty asm hides the constant, so it is not rebuilt per block).
     i32x8 ones;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
@@ -211,214 +249,260 @@ __global__ void __launch_bounds__(512, 2) fp8_causal_fwd(Fp8Params a) {
         asm volatile("" : "+v"(one4));
         ones[i] = one4;
     }
+    // The A-side E8M0 scale of the P.V MFMAs (127 = 2^0), set once here under a
+    // full EXEC mask: matrix instructions read every lane's scale byte whatever
+    // EXEC is, so the constant must never be materialised inside divergent code.
+    int sa = 127;
+    asm volatile("" : "+v"(sa));
 
-    // ---- matrix phase work.  Operands are double-buffered: the LDS reads for the
-    // next MFMA are issued before the current one, so LDS latency hides behind the
-    // 64-cycle matrix instructions instead of stalling each of them.
-    auto read_v = [&](const ATTN_LDS uint8_t* Vs, int dt) {
-        i32x8 va;
-#pragma unroll
-        for (int cc = 0; cc < 4; ++cc) {
-            i32x2 t = lds_read_tr8(Vs + (voff[cc] ^ (32 * dt)));
-            va[2 * cc] = t[0];
-            va[2 * cc + 1] = t[1];
-        }
-        return va;
-    };
-    auto read_k = [&](const ATTN_LDS uint8_t* Ks, int half, int kk) {
-        const ATTN_LDS uint8_t* kp = Ks + (c + 32 * half) * T::K_STRIDE + 64 * kk + 32 * hh;
-        i32x4 lo = lds_load16(kp), hi = lds_load16(kp + 16);
+    auto read32 = [&](const ATTN_LDS uint8_t* p) {
+        i32x4 lo = lds_load16(p), hi = lds_load16(p + 16);
         return i32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
     };
-    // S^T = K . Q^T for keys [0,32) (s0) and [32,64) (s1) of block j
-    auto qk = [&](int j) {
-        const ATTN_LDS uint8_t* Ks = smem + (j % 3) * T::STAGE;
-        i32x8 k0 = read_k(Ks, 0, 0), k1 = read_k(Ks, 1, 0);
+    // S^T = K . Q^T of block j for one half (K slot j%3): keys [0,32) in s0, [32,64) in s1.
+    auto qk = [&](int j, const i32x8 (&qr)[T::NKK], f32x16& s0, f32x16& s1) {
+        const ATTN_LDS uint8_t* kp = smem + (j % 3) * T::K_BYTES + c * T::K_STRIDE + 32 * hh;
         s0 = f32x16{0};
         s1 = f32x16{0};
 #pragma unroll
         for (int kk = 0; kk < T::NKK; ++kk) {
-            s0 = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(k0, qreg[kk], s0, 0, 0, 0, 0, 0, 0);
-            if (kk + 1 < T::NKK) k0 = read_k(Ks, 0, kk + 1);
-            s1 = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(k1, qreg[kk], s1, 0, 0, 0, 0, 0, 0);
-            if (kk + 1 < T::NKK) k1 = read_k(Ks, 1, kk + 1);
+            s0 = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(read32(kp + 64 * kk), qr[kk], s0,
+                                                                  0, 0, 0, 0, 0, 0);
+            s1 = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(read32(kp + 32 * T::K_STRIDE + 64 * kk),
+                                                                  qr[kk], s1, 0, 0, 0, 0, 0, 0);
         }
     };
-    // O^T += V^T . P^T (scaled) and L += 1 . P^T (scaled) for block j
-    auto pvmma = [&](int j) {
-        const ATTN_LDS uint8_t* Vs = smem + (j % 3) * T::STAGE + T::K_BYTES;
-        i32x8 va0 = read_v(Vs, 0), va1 = read_v(Vs, 1);
-        o[0] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(va0, pv, o[0], 0, 0, 0, 127, 0, scale_b);
-        va0 = read_v(Vs, 2);
-        o[1] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(va1, pv, o[1], 0, 0, 0, 127, 0, scale_b);
-        va1 = read_v(Vs, 3);
-        o[2] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(va0, pv, o[2], 0, 0, 0, 127, 0, scale_b);
-        o[3] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(va1, pv, o[3], 0, 0, 0, 127, 0, scale_b);
-        lacc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(ones, pv, lacc, 0, 0, 0, 127, 0, scale_b);
+    // O^T += V^T . P^T and L += 1 . P^T of block j for one half, both scaled by the
+    // E8M0 byte sb (V^T slot j%3): lane (d row c, half hh) reads V^T row 32dt + c,
+    // positions [32hh, +32).
+    auto pv = [&](int j, const i32x8& pvv, int sb, f32x16 (&o)[4], f32x16& l) {
+        const ATTN_LDS uint8_t* vp = smem + T::OFF_VT + (j % 3) * T::VT_BYTES + c * T::VT_STRIDE + 32 * hh;
+#pragma unroll
+        for (int dt = 0; dt < 4; ++dt) mfma_f8_scaled_acc(o[dt], read32(vp + 32 * dt * T::VT_STRIDE), pvv, sa, sb);
+        mfma_f8_scaled_acc(l, ones, pvv, sa, sb);
     };
-    // ---- probabilities of block j (vector unit): mask, block exponent, lazy reference, P bytes
-    auto softmax = [&](int j) {
-        // causal / tail mask, only on blocks that reach past the wave's first query:
+
+    // ---- probabilities of block j for one half: mask (diagonal blocks), block
+    // exponent M, e4m3 bytes.  Independent of the running reference.  Written as
+    // stages so the fully visible loop can spread them over the MFMAs of a phase.
+    auto prob_mask = [&](int j, int qabs, f32x16& s0, f32x16& s1) {
         // key kb0 + off(r) + 4hh is visible iff off(r) <= min(qabs, S-1) - kb0 - 4hh
-        const int kb0 = j * KB;
-        if (kb0 + KB - 1 > qw0) {
-            const int lim = min(qabs, S - 1) - kb0 - 4 * hh;
+        const int lim = min(qabs, S - 1) - j * KB - 4 * hh;
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int off = 8 * (r >> 2) + (r & 3);
-                s0[r] = off <= lim ? s0[r] : -INFINITY;
-                s1[r] = off + 32 <= lim ? s1[r] : -INFINITY;
-            }
+        for (int r = 0; r < 16; ++r) {
+            const int off = 8 * (r >> 2) + (r & 3);
+            s0[r] = off <= lim ? s0[r] : -INFINITY;
+            s1[r] = off + 32 <= lim ? s1[r] : -INFINITY;
         }
-        // block exponent M = ceil(max t)
-        float mx = -INFINITY;
+    };
+    auto prob_max = [&](const f32x16& s0, const f32x16& s1, int r0, int r1, float& mx) {
 #pragma unroll
-        for (int r = 0; r < 16; ++r) mx = fmaxf(fmaxf(mx, s0[r]), s1[r]);
+        for (int r = r0; r < r1; ++r) mx = fmaxf(fmaxf(mx, s0[r]), s1[r]);
+    };
+    // block exponent M and the per-row bias of the probability formula
+    auto prob_exponent = [&](float mx, float& M, float& bias) {
         mx = fmaxf(mx, other_half(mx));
-        const float M = fmaxf(ceilf(mx * a.c), -1.0e30f);  // floor: rows with no visible key here
-        // lazy power-of-two reference
+        M = fmaxf(ceilf(mx * a.c), -1.0e30f);  // floor: rows with no visible key here
+        bias = PMODE == 0 ? 8.0f - M : 120.0f - 8.0f * M;
+    };
+    // bytes of the 4 scores x[4q4 .. 4q4+3]: one packed dword of the P operand
+    auto prob_bytes = [&](const f32x16& x, int q4, float bias) -> int {
+        if (PMODE == 0) {
+            const float p0 = __builtin_amdgcn_exp2f(fmaf(x[4 * q4 + 0], a.c, bias));
+            const float p1 = __builtin_amdgcn_exp2f(fmaf(x[4 * q4 + 1], a.c, bias));
+            const float p2 = __builtin_amdgcn_exp2f(fmaf(x[4 * q4 + 2], a.c, bias));
+            const float p3 = __builtin_amdgcn_exp2f(fmaf(x[4 * q4 + 3], a.c, bias));
+            const int wd = __builtin_amdgcn_cvt_pk_fp8_f32(p0, p1, 0, false);
+            return __builtin_amdgcn_cvt_pk_fp8_f32(p2, p3, wd, true);
+        } else {
+            unsigned wd = 0;
+            wd = __builtin_amdgcn_cvt_pk_u8_f32(fmaf(x[4 * q4 + 0], a.a8, bias), 0, wd);
+            wd = __builtin_amdgcn_cvt_pk_u8_f32(fmaf(x[4 * q4 + 1], a.a8, bias), 1, wd);
+            wd = __builtin_amdgcn_cvt_pk_u8_f32(fmaf(x[4 * q4 + 2], a.a8, bias), 2, wd);
+            wd = __builtin_amdgcn_cvt_pk_u8_f32(fmaf(x[4 * q4 + 3], a.a8, bias), 3, wd);
+            return (int)wd;
+        }
+    };
+    auto probs = [&](int j, int qabs, f32x16& s0, f32x16& s1, bool masked, float& M, i32x8& pvv) {
+        if (masked) prob_mask(j, qabs, s0, s1);
+        float mx = -INFINITY, bias;
+        prob_max(s0, s1, 0, 16, mx);
+        prob_exponent(mx, M, bias);
+        pvv = i32x8{prob_bytes(s0, 0, bias), prob_bytes(s0, 1, bias), prob_bytes(s0, 2, bias),
+                    prob_bytes(s0, 3, bias), prob_bytes(s1, 0, bias), prob_bytes(s1, 1, bias),
+                    prob_bytes(s1, 2, bias), prob_bytes(s1, 3, bias)};
+    };
+
+    // Lazy power-of-two reference of one half: it moves (an exact rescale of that
+    // half's O and L) only when the block exponent exceeds it by more than
+    // kRefSlack; then the E8M0 scale of the block.
+    auto commit = [&](float M, float& ref, f32x16 (&o)[4], f32x16& l, int& sb) {
         const bool need = M > ref + kRefSlack;
         if (__ballot(need)) {
-            const float nref = need ? M : ref;
-            const float f = need ? __builtin_amdgcn_exp2f(ref - nref) : 1.0f;
+            acc_settle(o, l);
+            const float nr = need ? M : ref;
+            const float f = need ? __builtin_amdgcn_exp2f(ref - nr) : 1.0f;
 #pragma unroll
             for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
                 for (int r = 0; r < 16; ++r) o[dt][r] *= f;
 #pragma unroll
-            for (int r = 0; r < 16; ++r) lacc[r] *= f;
-            ref = nref;
+            for (int r = 0; r < 16; ++r) l[r] *= f;
+            acc_settle(o, l);   // the rescaled values are back before the next MFMA reads them
+            ref = nr;
         }
-        scale_b = (int)fminf(fmaxf(M - 8.0f - ref, -127.0f), 127.0f) + 127;
-        int pw[8];
-        if (PMODE == 0) {
-            const float bias = 8.0f - M;
-#pragma unroll
-            for (int q4 = 0; q4 < 4; ++q4) {
-                float p0 = __builtin_amdgcn_exp2f(fmaf(s0[4 * q4 + 0], a.c, bias));
-                float p1 = __builtin_amdgcn_exp2f(fmaf(s0[4 * q4 + 1], a.c, bias));
-                float p2 = __builtin_amdgcn_exp2f(fmaf(s0[4 * q4 + 2], a.c, bias));
-                float p3 = __builtin_amdgcn_exp2f(fmaf(s0[4 * q4 + 3], a.c, bias));
-                int wd = __builtin_amdgcn_cvt_pk_fp8_f32(p0, p1, 0, false);
-                pw[q4] = __builtin_amdgcn_cvt_pk_fp8_f32(p2, p3, wd, true);
-                p0 = __builtin_amdgcn_exp2f(fmaf(s1[4 * q4 + 0], a.c, bias));
-                p1 = __builtin_amdgcn_exp2f(fmaf(s1[4 * q4 + 1], a.c, bias));
-                p2 = __builtin_amdgcn_exp2f(fmaf(s1[4 * q4 + 2], a.c, bias));
-                p3 = __builtin_amdgcn_exp2f(fmaf(s1[4 * q4 + 3], a.c, bias));
-                wd = __builtin_amdgcn_cvt_pk_fp8_f32(p0, p1, 0, false);
-                pw[4 + q4] = __builtin_amdgcn_cvt_pk_fp8_f32(p2, p3, wd, true);
-            }
-        } else {
-            const float bc = 120.0f - 8.0f * M;
-#pragma unroll
-            for (int q4 = 0; q4 < 4; ++q4) {
-                unsigned wd = 0;
-                wd = __builtin_amdgcn_cvt_pk_u8_f32(fmaf(s0[4 * q4 + 0], a.a8, bc), 0, wd);
-                wd = __builtin_amdgcn_cvt_pk_u8_f32(fmaf(s0[4 * q4 + 1], a.a8, bc), 1, wd);
-                wd = __builtin_amdgcn_cvt_pk_u8_f32(fmaf(s0[4 * q4 + 2], a.a8, bc), 2, wd);
-                wd = __builtin_amdgcn_cvt_pk_u8_f32(fmaf(s0[4 * q4 + 3], a.a8, bc), 3, wd);
-                pw[q4] = (int)wd;
-                wd = 0;
-                wd = __builtin_amdgcn_cvt_pk_u8_f32(fmaf(s1[4 * q4 + 0], a.a8, bc), 0, wd);
-                wd = __builtin_amdgcn_cvt_pk_u8_f32(fmaf(s1[4 * q4 + 1], a.a8, bc), 1, wd);
-                wd = __builtin_amdgcn_cvt_pk_u8_f32(fmaf(s1[4 * q4 + 2], a.a8, bc), 2, wd);
-                wd = __builtin_amdgcn_cvt_pk_u8_f32(fmaf(s1[4 * q4 + 3], a.a8, bc), 3, wd);
-                pw[4 + q4] = (int)wd;
-            }
-        }
-        pv = i32x8{pw[0], pw[1], pw[2], pw[3], pw[4], pw[5], pw[6], pw[7]};
+        sb = (int)fminf(fmaxf(M - 8.0f - ref, -127.0f), 127.0f) + 127;
     };
 
-    // ---- schedule.  Every wave walks all nblk staged blocks: a block wholly above
-    // a wave's queries is fully masked, gives p = 0 and adds exactly nothing, and
-    // keeping the work uniform leaves each group's loop one straight path (the few
-    // extra diagonal MFMAs would otherwise be idle barrier time).  The two groups
-    // run separate loops with the same number of barriers:
-    //   iteration j, phase A: group 0 P.V(j-1) + S^T(j)   group 1 softmax(j-1)
-    //                phase B: group 0 softmax(j)          group 1 P.V(j-1) + S^T(j)
-    // All waves stage tile j+1 into the ring and issue the loads of tile j+2 at
-    // the start of phase A.
-    // A phase boundary: a workgroup barrier that the compiler may not schedule
-    // any instruction across, so each phase's work stays inside its phase.
-    auto phase_barrier = [&]() {
-        __builtin_amdgcn_sched_barrier(0);
-        __syncthreads();
-        __builtin_amdgcn_sched_barrier(0);
-    };
-    auto stage = [&](int j) {
-        if (j + 1 < nblk) lstore(j + 1);
-        if (j + 2 < nblk) gload(j + 2);
-    };
+    // ---- pipeline.  Entering iteration j: S^T(A, j) in sa0/sa1; P(B, j-1) in pb with
+    // scale sbb; K(j), K(j+1) and V^T(j) in LDS, V(j+1) in staging slot (j+1)%2,
+    // registers hold tile j+2.
+    f32x16 sa0, sa1, sb0, sb1;
+    i32x8 pa, pb = i32x8{0, 0, 0, 0, 0, 0, 0, 0};
+    int sba = 127, sbb = 127;
     gload(0);
     lstore(0);
-    if (nblk > 1) gload(1);
-    phase_barrier();
-
-    if (grp == 0) {
-        stage(0);
-        __builtin_amdgcn_s_setprio(1);
-        qk(0);
-        __builtin_amdgcn_s_setprio(0);
-        phase_barrier();
-        softmax(0);
-        phase_barrier();
-        for (int j = 1; j < nblk; ++j) {
-            stage(j);
-            __builtin_amdgcn_s_setprio(1);
-            pvmma(j - 1);
-            qk(j);
-            __builtin_amdgcn_s_setprio(0);
-            phase_barrier();
-            softmax(j);
-            phase_barrier();
-        }
-        pvmma(nblk - 1);
-        phase_barrier();
-    } else {
-        stage(0);
-        phase_barrier();
-        __builtin_amdgcn_s_setprio(1);
-        qk(0);
-        __builtin_amdgcn_s_setprio(0);
-        phase_barrier();
-        for (int j = 1; j < nblk; ++j) {
-            stage(j);
-            softmax(j - 1);
-            phase_barrier();
-            __builtin_amdgcn_s_setprio(1);
-            pvmma(j - 1);
-            qk(j);
-            __builtin_amdgcn_s_setprio(0);
-            phase_barrier();
-        }
-        softmax(nblk - 1);
-        phase_barrier();
-        pvmma(nblk - 1);
+    if (nblk > 1) {
+        gload(1);
+        lstore(1);
     }
+    if (nblk > 2) gload(2);
+    __syncthreads();
+    transpose_v(0);
+    qk(0, qa, sa0, sa1);
+    __syncthreads();
 
-    // ---- epilogue: out = bf16(v_scale * (O / L)), lane holds query c, d = 32dt + 8(r/4) + 4hh + r%4
-    if (qabs < S) {
-        const float lsum = lacc[0];
-        __bf16* op = a.o + (((int64_t)b * S + qabs) * a.Hq + h) * 128;
+    // Blocks [1, jfast) are fully visible to every wave of the workgroup and have all
+    // neighbours in range: they run the branch-free body.  The rest (block 0, the
+    // diagonal blocks, the pipeline tail) run the general body, which always applies
+    // the causal mask (a no-op on the few fully visible blocks it sees).
+    int jfast = max(1, min(nblk - 3, q0 / KB));
+    asm volatile("" : "+s"(jfast));   // opaque bound: keep the fast loop a loop of its own
+    // General body (block 0, diagonal blocks, pipeline tail): masked, with every
+    // staging step guarded.  Score MFMAs come first in each phase: the tile they
+    // produce is read by the vector code of the next phase.
+    auto iteration = [&](int j) {
+        float Ma, Mb;
+        // phase 1
+        qk(j, qb, sb0, sb1);
+        if (j >= 1) pv(j - 1, pb, sbb, ob, lb);
+        probs(j, qA, sa0, sa1, true, Ma, pa);
+        if (j + 1 < nblk) transpose_v(j + 1);
+        commit(Ma, refa, oa, la, sba);
+        // phase 2
+        if (j + 1 < nblk) qk(j + 1, qa, sa0, sa1);
+        pv(j, pa, sba, oa, la);
+        probs(j, qB, sb0, sb1, true, Mb, pb);
+        if (j + 2 < nblk) lstore(j + 2);
+        if (j + 3 < nblk) gload(j + 3);
+        commit(Mb, refb, ob, lb, sbb);
+        block_sync();
+    };
+
+    // One phase of the fully visible loop as an explicit instruction order: slot i
+    // issues the LDS reads of the operand two MFMAs ahead, MFMA i, a share of the
+    // probability stages of the other half and any staging work, and ends in a
+    // scheduling fence.  MFMAs 0 .. NS-1 compute S^T of block jk into (so0, so1);
+    // MFMAs NS .. NS+4 accumulate P.V and the row sum of block jv from pin with
+    // scale sbin; the vector work turns (si0, si1) into the bytes and exponent of the
+    // next P.
+    constexpr int NS = 2 * T::NKK;      // score MFMAs per phase
+    constexpr int NM = NS + 5;          // all MFMAs per phase
+    constexpr int NSTAGE = 11;          // 2 max, exponent, 8 byte groups
+    auto fast_phase = [&](int jk, const i32x8 (&qr)[T::NKK], f32x16& so0, f32x16& so1, int jv,
+                          const i32x8& pin, int sbin, f32x16 (&o)[4], f32x16& l, f32x16& si0, f32x16& si1,
+                          float& M, i32x8& pout, auto&& extra) {
+        const ATTN_LDS uint8_t* kp = smem + (jk % 3) * T::K_BYTES + c * T::K_STRIDE + 32 * hh;
+        const ATTN_LDS uint8_t* vp = smem + T::OFF_VT + (jv % 3) * T::VT_BYTES + c * T::VT_STRIDE + 32 * hh;
+        i32x8 op[NS + 4];
+        auto rd = [&](int i) {
+            if (i < NS) op[i] = read32(kp + (i & 1) * 32 * T::K_STRIDE + 64 * (i >> 1));
+            else if (i < NS + 4) op[i] = read32(vp + 32 * (i - NS) * T::VT_STRIDE);
+        };
+        float mx = -INFINITY, bias = 0.0f;
+        int pw[8];
+        rd(0);
+        rd(1);
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int dt = 0; dt < 4; ++dt) {
+        for (int i = 0; i < NM; ++i) {
+            rd(i + 2);
+            if (i < NS) {
+                f32x16& sd = (i & 1) ? so1 : so0;
+                sd = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(op[i], qr[i >> 1], i < 2 ? f32x16{0} : sd,
+                                                                      0, 0, 0, 0, 0, 0);
+            } else if (i < NS + 4) {
+                mfma_f8_scaled_acc(o[i - NS], op[i], pin, sa, sbin);
+            } else {
+                mfma_f8_scaled_acc(l, ones, pin, sa, sbin);
+            }
 #pragma unroll
-            for (int r4 = 0; r4 < 4; ++r4) {
-                float x0 = (o[dt][4 * r4 + 0] / lsum) * a.v_scale;
-                float x1 = (o[dt][4 * r4 + 1] / lsum) * a.v_scale;
-                float x2 = (o[dt][4 * r4 + 2] / lsum) * a.v_scale;
-                float x3 = (o[dt][4 * r4 + 3] / lsum) * a.v_scale;
-                uint2 pk = make_uint2(pack_bf16x2(x0, x1), pack_bf16x2(x2, x3));
-                *reinterpret_cast<uint2*>(op + 32 * dt + 8 * r4 + 4 * hh) = pk;
+            for (int st = (i * NSTAGE) / NM; st < ((i + 1) * NSTAGE) / NM; ++st) {
+                if (st == 0) prob_max(si0, si1, 0, 8, mx);
+                else if (st == 1) prob_max(si0, si1, 8, 16, mx);
+                else if (st == 2) prob_exponent(mx, M, bias);
+                else {
+                    pw[st - 3] = prob_bytes((st - 3) < 4 ? si0 : si1, (st - 3) & 3, bias);
+                    asm volatile("" : "+v"(pw[st - 3]));   // computed here, not sunk to its use
+                }
+            }
+            extra(i);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        pout = i32x8{pw[0], pw[1], pw[2], pw[3], pw[4], pw[5], pw[6], pw[7]};
+    };
+    // Fully visible block j with every neighbour in range.
+    auto fast_iteration = [&](int j) {
+        float Ma, Mb;
+        fast_phase(j, qb, sb0, sb1, j - 1, pb, sbb, ob, lb, sa0, sa1, Ma, pa, [&](int i) {
+            if (i == 0) transpose_read(j + 1);
+            if (i == NM / 2) transpose_write(j + 1);
+        });
+        commit(Ma, refa, oa, la, sba);
+        fast_phase(j + 1, qa, sa0, sa1, j, pa, sba, oa, la, sb0, sb1, Mb, pb, [&](int i) {
+            if (i == 1) lstore(j + 2);
+            if (i == 2) gload(j + 3);
+        });
+        commit(Mb, refb, ob, lb, sbb);
+        block_sync();
+    };
+    iteration(0);
+    for (int j = 1; j < jfast; ++j) fast_iteration(j);
+    for (int j = jfast; j < nblk; ++j) iteration(j);
+    pv(nblk - 1, pb, sbb, ob, lb);
+    // The matrix instructions ignore EXEC: settling the accumulators here also keeps
+    // all matrix work (and any operand copies it needs) out of the divergent stores.
+    acc_settle(oa, la);
+    acc_settle(ob, lb);
+
+    // ---- epilogue: out = bf16(v_scale * (O / L)), lane holds query c of a half,
+    // d = 32dt + 8(r/4) + 4hh + r%4
+    auto store = [&](int qabs, const f32x16 (&o)[4], const f32x16& l) {
+        if (qabs < S) {
+            const float lsum = l[0];
+            __bf16* op = a.o + (((int64_t)b * S + qabs) * a.Hq + h) * 128;
+#pragma unroll
+            for (int dt = 0; dt < 4; ++dt) {
+#pragma unroll
+                for (int r4 = 0; r4 < 4; ++r4) {
+                    float x0 = (o[dt][4 * r4 + 0] / lsum) * a.v_scale;
+                    float x1 = (o[dt][4 * r4 + 1] / lsum) * a.v_scale;
+                    float x2 = (o[dt][4 * r4 + 2] / lsum) * a.v_scale;
+                    float x3 = (o[dt][4 * r4 + 3] / lsum) * a.v_scale;
+                    uint2 pk = make_uint2(pack_bf16x2(x0, x1), pack_bf16x2(x2, x3));
+                    *reinterpret_cast<uint2*>(op + 32 * dt + 8 * r4 + 4 * hh) = pk;
+                }
             }
         }
-    }
+    };
+    store(qA, oa, la);
+    store(qB, ob, lb);
 }
 
 template <int DQK, int PMODE>
 hipError_t launch_t(const Problem& p) {
-    constexpr int NW = 8;
-    constexpr int BM = NW * 32;
+    constexpr int NW = 4;
+    constexpr int BM = NW * 64;
     Fp8Params a;
     a.q = static_cast<const uint8_t*>(p.q);
     a.k = static_cast<const uint8_t*>(p.k);

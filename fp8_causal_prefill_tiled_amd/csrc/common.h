@@ -58,6 +58,40 @@ __device__ __forceinline__ i16x8 i16x8_cat(i16x4 a, i16x4 b) {
     return i16x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
 }
 
+// Force accumulators to be materialised at this point in uniform control flow
+// (an empty asm that reads and writes them cannot be moved or sunk into a branch).
+__device__ __forceinline__ void pin_all(f32x16 (&o)[4], f32x16& l) {
+    asm volatile("" : "+v"(o[0]), "+v"(o[1]), "+v"(o[2]), "+v"(o[3]), "+v"(l));
+}
+
+// acc += A . B on the FP8 matrix cores (32x32x64, e4m3 operands) with per-lane E8M0
+// scales: A's byte from scale_a, B's from scale_b.  The accumulator lives in the
+// accumulation (AGPR) half of the register file, so score tiles computed by
+// compiler-generated MFMAs can take VGPRs that vector code reads directly.
+__device__ __forceinline__ void mfma_f8_scaled_acc(f32x16& acc, const i32x8& a, const i32x8& b, int scale_a,
+                                                   int scale_b) {
+    asm("v_mfma_scale_f32_32x32x64_f8f6f4 %0, %1, %2, %0, %3, %4 op_sel_hi:[0,0,0]"
+        : "+a"(acc)
+        : "v"(a), "v"(b), "v"(scale_a), "v"(scale_b));
+}
+
+// Before any other instruction touches accumulators written by mfma_f8_scaled_acc:
+// a 16-pass MFMA needs independent cycles before its result may be read, which
+// the compiler does not insert for inline asm.  24 wait states cover the 16-pass
+// XDL-write-to-read requirement.  Being volatile and tied to every accumulator,
+// this also keeps all of those MFMAs in uniform control flow ahead of it.
+__device__ __forceinline__ void acc_settle(f32x16 (&o)[4], f32x16& l) {
+    asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+a"(o[0]), "+a"(o[1]), "+a"(o[2]), "+a"(o[3]), "+a"(l));
+}
+
+// Fence the scheduler on both sides of a workgroup barrier: without it, ALU and
+// matrix instructions that do not touch memory may be moved across s_barrier.
+__device__ __forceinline__ void block_sync() {
+    __builtin_amdgcn_sched_barrier(0);
+    __syncthreads();
+    __builtin_amdgcn_sched_barrier(0);
+}
+
 __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
     __bf16 x = (__bf16)a, y = (__bf16)b;
     return (uint32_t)__builtin_bit_cast(uint16_t, x) | ((uint32_t)__builtin_bit_cast(uint16_t, y) << 16);
