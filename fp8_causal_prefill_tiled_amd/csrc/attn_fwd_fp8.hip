@@ -25,6 +25,8 @@
 // of O^T = V^T . P^T.  V^T comes straight from LDS with the transposing
 // ds_read_b64_tr_b8.  K and V blocks are staged HBM -> registers -> LDS with
 // 16-byte coalesced loads, double-buffered, one barrier per block.
+#include <type_traits>
+
 #include "common.h"
 #include "launch.h"
 
@@ -42,10 +44,10 @@ struct Fp8Tile {
     static constexpr int V_BYTES = KB * 128;      // key-major V staging tile, chunk-swizzled
     static constexpr int VT_STRIDE = KB + 16;     // padded LDS row of V^T (one d, 64 keys), bytes
     static constexpr int VT_BYTES = 128 * VT_STRIDE;
-    // LDS: 3 K slots, 3 V^T slots, 2 key-major V staging tiles
+    // LDS: 3 slots each of K, V^T and the key-major V staging tile; block j uses slot j%3
     static constexpr int OFF_VT = 3 * K_BYTES;
     static constexpr int OFF_VS = OFF_VT + 3 * VT_BYTES;
-    static constexpr int LDS_BYTES = OFF_VS + 2 * V_BYTES;
+    static constexpr int LDS_BYTES = OFF_VS + 3 * V_BYTES;
     static constexpr int K_CHUNKS = KB * DQK / 16;
     static constexpr int V_CHUNKS = KB * 128 / 16;
 };
@@ -73,24 +75,26 @@ __device__ __forceinline__ int v_swz(int row) { return (row & 3) | (((row >> 3) 
 // rows of one head; wave w owns rows [64w, 64w + 64) of the tile as two 32-row
 // halves A and B.  Each iteration j is two phases whose matrix and vector work
 // are independent of each other:
-//     phase 1:  MFMA  P.V of half B, block j-1  and  S^T of half B, block j
+//     phase 1:  MFMA  S^T of half B, block j  and  P.V of half B, block j-1
 //               VALU  probabilities of half A, block j
 //     phase 2:  MFMA  S^T of half A, block j+1  and  P.V of half A, block j
 //               VALU  probabilities of half B, block j
 // This is the pages' two-wave ping-pong ("Two-wave ping-pong schedule", Zyphra
 // ZYFA page, MarkTechPost) moved inside one wave: the two halves take the roles
-// of the two waves, and within a phase the scheduler interleaves each 64-cycle
-// 32x32x64 MFMA with the ~10 vector instructions that gfx950 issues in its
-// shadow from the same wave.  Only two score tiles are live at any time.
+// of the two waves.  In the fully visible loop every phase is issued as fixed
+// slots (the LDS reads of the operand two MFMAs ahead, one MFMA, about ten vector
+// instructions), the number a 64-cycle 32x32x64 MFMA hides on gfx950 when one
+// wave runs per SIMD.  Only two score tiles are live at any time.
 //
-// LDS.  K tiles (row-major, padded rows) and V^T tiles each live in 3 slots; V^T
-// row d holds the block's 64 keys in the byte order of the probability operand,
-// so both matrix operands are plain 16-byte LDS reads.  V^T is built once per
-// workgroup from a key-major staging tile (2 slots) with the transposing
-// ds_read_b64_tr_b8, which is far slower per byte than ds_read_b128 on gfx950,
-// so it is paid once per tile rather than once per wave.  Iteration j builds
-// V^T(j+1), stores K(j+2) and V(j+2) from registers and issues the global loads
-// of tile j+3; one barrier ends the iteration.
+// LDS.  K tiles (row-major, padded rows), V^T tiles and key-major V staging tiles
+// each live in 3 slots, block j in slot j%3; the fully visible loop is unrolled
+// three times so every LDS address is a per-lane base plus a constant.  V^T row
+// d holds the block's 64 keys in the byte order of the probability operand, so
+// both matrix operands are plain 16-byte LDS reads; it is built once per
+// workgroup with the transposing ds_read_b64_tr_b8, which is far slower per byte
+// than ds_read_b128 on gfx950.  Iteration j builds V^T(j+1), stores K(j+2) and
+// V(j+2) from registers and issues the buffer loads of block j+3 (rows past S
+// read as zeros); one barrier ends the iteration.
 template <int DQK, int PMODE>
 __global__ void __launch_bounds__(256, 1) fp8_causal_fwd(Fp8Params a) {
     using T = Fp8Tile<DQK>;
@@ -127,8 +131,8 @@ __global__ void __launch_bounds__(256, 1) fp8_causal_fwd(Fp8Params a) {
     const int qB = qw0 + 32 + c;                  // and in half B
 
     const int64_t q_row = (int64_t)a.Hq * DQK;
-    const int64_t k_row = (int64_t)a.Hkv * DQK;
-    const int64_t v_row = (int64_t)a.Hkv * 128;
+    const int k_row = a.Hkv * DQK;                // bytes between consecutive keys
+    const int v_row = a.Hkv * 128;
     const uint8_t* kbase = a.k + (int64_t)b * S * k_row + (int64_t)g * DQK;
     const uint8_t* vbase = a.v + (int64_t)b * S * v_row + (int64_t)g * 128;
 
@@ -147,50 +151,44 @@ __global__ void __launch_bounds__(256, 1) fp8_causal_fwd(Fp8Params a) {
     load_q(qA, qa);
     load_q(qB, qb);
 
-    // ---- staging: global -> registers two iterations ahead (gload), registers -> LDS (lstore).
-    // Rows past S are clamped to row S-1: they are loaded in bounds, their scores are
-    // always masked and their probabilities are exactly zero, so the load is branch-free.
+    // ---- staging: HBM -> registers (gload, one buffer resource per block whose range
+    // ends at row S, so rows past S read as zeros), registers -> LDS slot (lstore).
     i32x4 kst[KPT];
     i32x4 vst[VPT];
+    int kgo[KPT], vgo[VPT];     // per-lane byte offsets of the staged chunks inside a block
+    int kso[KPT], vso[VPT];     // and their LDS offsets inside a slot
+#pragma unroll
+    for (int i = 0; i < KPT; ++i) {
+        const int idx = min(tid + i * NT, T::K_CHUNKS - 1);
+        const int row = idx / KCH_ROW, cc = idx % KCH_ROW;
+        kgo[i] = row * k_row + 16 * cc;
+        kso[i] = row * T::K_STRIDE + 16 * cc;
+    }
+#pragma unroll
+    for (int i = 0; i < VPT; ++i) {
+        const int idx = tid + i * NT;
+        const int row = idx >> 3, cc = idx & 7;
+        vgo[i] = row * v_row + 16 * cc;
+        vso[i] = row * 128 + 16 * (cc ^ v_swz(row));
+    }
     auto gload = [&](int j) {
+        const int rows = min(S - j * KB, KB);
+        const auto kr = buffer_rsrc(kbase + (int64_t)j * KB * k_row, rows * k_row);
+        const auto vr = buffer_rsrc(vbase + (int64_t)j * KB * v_row, rows * v_row);
 #pragma unroll
-        for (int i = 0; i < KPT; ++i) {
-            const int idx = tid + i * NT;
-            if (T::K_CHUNKS % NT == 0 || idx < T::K_CHUNKS) {
-                const int row = idx / KCH_ROW, cc = idx % KCH_ROW;
-                const int key = min(j * KB + row, S - 1);
-                kst[i] = load16(kbase + (int64_t)key * k_row + 16 * cc);
-            }
-        }
+        for (int i = 0; i < KPT; ++i)
+            if (T::K_CHUNKS % NT == 0 || tid + i * NT < T::K_CHUNKS) kst[i] = buffer_load16(kr, kgo[i]);
 #pragma unroll
-        for (int i = 0; i < VPT; ++i) {
-            const int idx = tid + i * NT;
-            if (T::V_CHUNKS % NT == 0 || idx < T::V_CHUNKS) {
-                const int row = idx >> 3, cc = idx & 7;
-                const int key = min(j * KB + row, S - 1);
-                vst[i] = load16(vbase + (int64_t)key * v_row + 16 * cc);
-            }
-        }
+        for (int i = 0; i < VPT; ++i) vst[i] = buffer_load16(vr, vgo[i]);
     };
-    auto lstore = [&](int j) {   // K(j) -> K slot j%3, V(j) -> staging slot j%2
-        ATTN_LDS uint8_t* Ks = smem + (j % 3) * T::K_BYTES;
-        ATTN_LDS uint8_t* Vs = smem + T::OFF_VS + (j & 1) * T::V_BYTES;
+    auto lstore = [&](int slot) {   // K -> K slot, V -> staging slot
+        ATTN_LDS uint8_t* Ks = smem + slot * T::K_BYTES;
+        ATTN_LDS uint8_t* Vs = smem + T::OFF_VS + slot * T::V_BYTES;
 #pragma unroll
-        for (int i = 0; i < KPT; ++i) {
-            const int idx = tid + i * NT;
-            if (T::K_CHUNKS % NT == 0 || idx < T::K_CHUNKS) {
-                const int row = idx / KCH_ROW, cc = idx % KCH_ROW;
-                lds_store16(Ks + row * T::K_STRIDE + 16 * cc, kst[i]);
-            }
-        }
+        for (int i = 0; i < KPT; ++i)
+            if (T::K_CHUNKS % NT == 0 || tid + i * NT < T::K_CHUNKS) lds_store16(Ks + kso[i], kst[i]);
 #pragma unroll
-        for (int i = 0; i < VPT; ++i) {
-            const int idx = tid + i * NT;
-            if (T::V_CHUNKS % NT == 0 || idx < T::V_CHUNKS) {
-                const int row = idx >> 3, cc = idx & 7;
-                lds_store16(Vs + row * 128 + 16 * (cc ^ v_swz(row)), vst[i]);
-            }
-        }
+        for (int i = 0; i < VPT; ++i) lds_store16(Vs + vso[i], vst[i]);
     };
 
     // ---- V^T construction: V^T row d holds the 64 keys at positions p = 32h + t in the
@@ -213,23 +211,19 @@ __global__ void __launch_bounds__(256, 1) fp8_causal_fwd(Fp8Params a) {
         tr_dst[u] = (dbase + n) * T::VT_STRIDE + p0;
     }
     i32x2 tlo[TPT], thi[TPT];
-    auto transpose_read = [&](int j) {   // staging slot j%2 -> registers
-        const ATTN_LDS uint8_t* Vs = smem + T::OFF_VS + (j & 1) * T::V_BYTES;
+    auto transpose_read = [&](int slot) {   // staging slot -> registers
+        const ATTN_LDS uint8_t* Vs = smem + T::OFF_VS + slot * T::V_BYTES;
 #pragma unroll
         for (int u = 0; u < TPT; ++u) {
             tlo[u] = lds_read_tr8(Vs + tr_off[u][0]);
             thi[u] = lds_read_tr8(Vs + tr_off[u][1]);
         }
     };
-    auto transpose_write = [&](int j) {   // registers -> V^T slot j%3
+    auto transpose_write = [&](int slot) {   // registers -> V^T slot
 #pragma unroll
         for (int u = 0; u < TPT; ++u)
-            lds_store16(smem + T::OFF_VT + (j % 3) * T::VT_BYTES + tr_dst[u],
+            lds_store16(smem + T::OFF_VT + slot * T::VT_BYTES + tr_dst[u],
                         i32x4{tlo[u][0], tlo[u][1], thi[u][0], thi[u][1]});
-    };
-    auto transpose_v = [&](int j) {
-        transpose_read(j);
-        transpose_write(j);
     };
 
     f32x16 oa[4], ob[4];
@@ -259,26 +253,45 @@ __global__ void __launch_bounds__(256, 1) fp8_causal_fwd(Fp8Params a) {
         i32x4 lo = lds_load16(p), hi = lds_load16(p + 16);
         return i32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
     };
-    // S^T = K . Q^T of block j for one half (K slot j%3): keys [0,32) in s0, [32,64) in s1.
-    auto qk = [&](int j, const i32x8 (&qr)[T::NKK], f32x16& s0, f32x16& s1) {
-        const ATTN_LDS uint8_t* kp = smem + (j % 3) * T::K_BYTES + c * T::K_STRIDE + 32 * hh;
+    // Matrix operands, read from LDS once per block and kept in registers for both
+    // halves.  op[i], i < NS, is a K operand of the score MFMAs (key half i%2, d step
+    // i/2); op[NS + dt] is the V^T operand of d rows [32dt, +32).  Lane (row c, half
+    // hh) reads 32 bytes at 32hh.  Phase 2 of iteration j reads K(j+1) and V^T(j);
+    // phase 1 of iteration j+1 reuses both (S^T of half B, block j+1 and P.V of half
+    // B, block j), so it issues no operand reads at all.
+    constexpr int NS = 2 * T::NKK;      // score MFMAs per phase
+    constexpr int NM = NS + 5;          // all MFMAs per phase
+    i32x8 op[NS + 4];
+    auto read_operand = [&](int kslot, int vslot, int i) {
+        if (i < NS)
+            op[i] = read32(smem + kslot * T::K_BYTES + c * T::K_STRIDE + 32 * hh + (i & 1) * 32 * T::K_STRIDE +
+                           64 * (i >> 1));
+        else if (i < NS + 4)
+            op[i] = read32(smem + T::OFF_VT + vslot * T::VT_BYTES + (32 * (i - NS) + c) * T::VT_STRIDE + 32 * hh);
+    };
+    auto read_k = [&](int kslot) {
+#pragma unroll
+        for (int i = 0; i < NS; ++i) read_operand(kslot, 0, i);
+    };
+    auto read_v = [&](int vslot) {
+#pragma unroll
+        for (int i = NS; i < NS + 4; ++i) read_operand(0, vslot, i);
+    };
+    // S^T = K . Q^T for one half from the kept K operands: keys [0,32) in s0, [32,64) in s1.
+    auto qk = [&](const i32x8 (&qr)[T::NKK], f32x16& s0, f32x16& s1) {
         s0 = f32x16{0};
         s1 = f32x16{0};
 #pragma unroll
         for (int kk = 0; kk < T::NKK; ++kk) {
-            s0 = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(read32(kp + 64 * kk), qr[kk], s0,
-                                                                  0, 0, 0, 0, 0, 0);
-            s1 = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(read32(kp + 32 * T::K_STRIDE + 64 * kk),
-                                                                  qr[kk], s1, 0, 0, 0, 0, 0, 0);
+            s0 = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(op[2 * kk], qr[kk], s0, 0, 0, 0, 0, 0, 0);
+            s1 = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(op[2 * kk + 1], qr[kk], s1, 0, 0, 0, 0, 0, 0);
         }
     };
-    // O^T += V^T . P^T and L += 1 . P^T of block j for one half, both scaled by the
-    // E8M0 byte sb (V^T slot j%3): lane (d row c, half hh) reads V^T row 32dt + c,
-    // positions [32hh, +32).
-    auto pv = [&](int j, const i32x8& pvv, int sb, f32x16 (&o)[4], f32x16& l) {
-        const ATTN_LDS uint8_t* vp = smem + T::OFF_VT + (j % 3) * T::VT_BYTES + c * T::VT_STRIDE + 32 * hh;
+    // O^T += V^T . P^T and L += 1 . P^T for one half from the kept V^T operands, both
+    // scaled by the E8M0 byte sb.
+    auto pv = [&](const i32x8& pvv, int sb, f32x16 (&o)[4], f32x16& l) {
 #pragma unroll
-        for (int dt = 0; dt < 4; ++dt) mfma_f8_scaled_acc(o[dt], read32(vp + 32 * dt * T::VT_STRIDE), pvv, sa, sb);
+        for (int dt = 0; dt < 4; ++dt) mfma_f8_scaled_acc(o[dt], op[NS + dt], pvv, sa, sb);
         mfma_f8_scaled_acc(l, ones, pvv, sa, sb);
     };
 
@@ -323,8 +336,8 @@ __global__ void __launch_bounds__(256, 1) fp8_causal_fwd(Fp8Params a) {
             return (int)wd;
         }
     };
-    auto probs = [&](int j, int qabs, f32x16& s0, f32x16& s1, bool masked, float& M, i32x8& pvv) {
-        if (masked) prob_mask(j, qabs, s0, s1);
+    auto probs = [&](int j, int qabs, f32x16& s0, f32x16& s1, float& M, i32x8& pvv) {
+        prob_mask(j, qabs, s0, s1);
         float mx = -INFINITY, bias;
         prob_max(s0, s1, 0, 16, mx);
         prob_exponent(mx, M, bias);
@@ -332,7 +345,6 @@ __global__ void __launch_bounds__(256, 1) fp8_causal_fwd(Fp8Params a) {
                     prob_bytes(s0, 3, bias), prob_bytes(s1, 0, bias), prob_bytes(s1, 1, bias),
                     prob_bytes(s1, 2, bias), prob_bytes(s1, 3, bias)};
     };
-
     // Lazy power-of-two reference of one half: it moves (an exact rescale of that
     // half's O and L) only when the block exponent exceeds it by more than
     // kRefSlack; then the E8M0 scale of the block.
@@ -355,8 +367,8 @@ __global__ void __launch_bounds__(256, 1) fp8_causal_fwd(Fp8Params a) {
     };
 
     // ---- pipeline.  Entering iteration j: S^T(A, j) in sa0/sa1; P(B, j-1) in pb with
-    // scale sbb; K(j), K(j+1) and V^T(j) in LDS, V(j+1) in staging slot (j+1)%2,
-    // registers hold tile j+2.
+    // scale sbb; op holds K(j) and V^T(j-1); LDS holds K(j+1) and V^T(j), staging slot
+    // (j+1)%3 holds V(j+1); registers hold block j+2.
     f32x16 sa0, sa1, sb0, sb1;
     i32x8 pa, pb = i32x8{0, 0, 0, 0, 0, 0, 0, 0};
     int sba = 127, sbb = 127;
@@ -368,65 +380,63 @@ __global__ void __launch_bounds__(256, 1) fp8_causal_fwd(Fp8Params a) {
     }
     if (nblk > 2) gload(2);
     __syncthreads();
-    transpose_v(0);
-    qk(0, qa, sa0, sa1);
+    transpose_read(0);
+    transpose_write(0);
+    read_k(0);
+    qk(qa, sa0, sa1);
     __syncthreads();
 
-    // Blocks [1, jfast) are fully visible to every wave of the workgroup and have all
-    // neighbours in range: they run the branch-free body.  The rest (block 0, the
-    // diagonal blocks, the pipeline tail) run the general body, which always applies
-    // the causal mask (a no-op on the few fully visible blocks it sees).
-    int jfast = max(1, min(nblk - 3, q0 / KB));
-    asm volatile("" : "+s"(jfast));   // opaque bound: keep the fast loop a loop of its own
-    // General body (block 0, diagonal blocks, pipeline tail): masked, with every
-    // staging step guarded.  Score MFMAs come first in each phase: the tile they
-    // produce is read by the vector code of the next phase.
+    // General body (block 0, diagonal blocks, pipeline tail, unroll remainder):
+    // masked, every staging step guarded, slots computed at run time.  Score MFMAs
+    // come first in each phase: the tile they produce is read by the vector code
+    // of the next phase.
     auto iteration = [&](int j) {
         float Ma, Mb;
-        // phase 1
-        qk(j, qb, sb0, sb1);
-        if (j >= 1) pv(j - 1, pb, sbb, ob, lb);
-        probs(j, qA, sa0, sa1, true, Ma, pa);
-        if (j + 1 < nblk) transpose_v(j + 1);
-        commit(Ma, refa, oa, la, sba);
-        // phase 2
-        if (j + 1 < nblk) qk(j + 1, qa, sa0, sa1);
-        pv(j, pa, sba, oa, la);
-        probs(j, qB, sb0, sb1, true, Mb, pb);
-        if (j + 2 < nblk) lstore(j + 2);
+        const int s0 = j % 3, s1 = (j + 1) % 3, s2 = (j + 2) % 3;
+        // phase 1: operands K(j), V^T(j-1) already in op
+        qk(qb, sb0, sb1);
+        if (j >= 1) pv(pb, sbb, ob, lb);
+        probs(j, qA, sa0, sa1, Ma, pa);
+        if (j + 1 < nblk) {
+            transpose_read(s1);
+            transpose_write(s1);
+        }
+        if (j + 2 < nblk) lstore(s2);
         if (j + 3 < nblk) gload(j + 3);
+        commit(Ma, refa, oa, la, sba);
+        // phase 2: read K(j+1), V^T(j)
+        if (j + 1 < nblk) {
+            read_k(s1);
+            qk(qa, sa0, sa1);
+        }
+        read_v(s0);
+        pv(pa, sba, oa, la);
+        probs(j, qB, sb0, sb1, Mb, pb);
         commit(Mb, refb, ob, lb, sbb);
         block_sync();
     };
 
     // One phase of the fully visible loop as an explicit instruction order: slot i
-    // issues the LDS reads of the operand two MFMAs ahead, MFMA i, a share of the
-    // probability stages of the other half and any staging work, and ends in a
-    // scheduling fence.  MFMAs 0 .. NS-1 compute S^T of block jk into (so0, so1);
-    // MFMAs NS .. NS+4 accumulate P.V and the row sum of block jv from pin with
-    // scale sbin; the vector work turns (si0, si1) into the bytes and exponent of the
-    // next P.
-    constexpr int NS = 2 * T::NKK;      // score MFMAs per phase
-    constexpr int NM = NS + 5;          // all MFMAs per phase
+    // issues (with `reads`) the LDS reads of the operand two MFMAs ahead, MFMA i, a
+    // share of the probability stages of the other half and any staging work, and
+    // ends in a scheduling fence.  MFMAs 0 .. NS-1 compute S^T into (so0, so1) from
+    // the K operands; MFMAs NS .. NS+4 accumulate P.V and the row sum from pin with
+    // scale sbin; the vector work turns (si0, si1) into the bytes and exponent of
+    // the next P.
     constexpr int NSTAGE = 11;          // 2 max, exponent, 8 byte groups
-    auto fast_phase = [&](int jk, const i32x8 (&qr)[T::NKK], f32x16& so0, f32x16& so1, int jv,
+    auto fast_phase = [&](bool reads, int ks, int vs, const i32x8 (&qr)[T::NKK], f32x16& so0, f32x16& so1,
                           const i32x8& pin, int sbin, f32x16 (&o)[4], f32x16& l, f32x16& si0, f32x16& si1,
                           float& M, i32x8& pout, auto&& extra) {
-        const ATTN_LDS uint8_t* kp = smem + (jk % 3) * T::K_BYTES + c * T::K_STRIDE + 32 * hh;
-        const ATTN_LDS uint8_t* vp = smem + T::OFF_VT + (jv % 3) * T::VT_BYTES + c * T::VT_STRIDE + 32 * hh;
-        i32x8 op[NS + 4];
-        auto rd = [&](int i) {
-            if (i < NS) op[i] = read32(kp + (i & 1) * 32 * T::K_STRIDE + 64 * (i >> 1));
-            else if (i < NS + 4) op[i] = read32(vp + 32 * (i - NS) * T::VT_STRIDE);
-        };
         float mx = -INFINITY, bias = 0.0f;
         int pw[8];
-        rd(0);
-        rd(1);
+        if (reads) {
+            read_operand(ks, vs, 0);
+            read_operand(ks, vs, 1);
+        }
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int i = 0; i < NM; ++i) {
-            rd(i + 2);
+            if (reads) read_operand(ks, vs, i + 2);
             if (i < NS) {
                 f32x16& sd = (i & 1) ? so1 : so0;
                 sd = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(op[i], qr[i >> 1], i < 2 ? f32x16{0} : sd,
@@ -436,6 +446,8 @@ __global__ void __launch_bounds__(256, 1) fp8_causal_fwd(Fp8Params a) {
             } else {
                 mfma_f8_scaled_acc(l, ones, pin, sa, sbin);
             }
+            // the MFMA issues first; the slot's vector work then runs in its shadow
+            __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
             for (int st = (i * NSTAGE) / NM; st < ((i + 1) * NSTAGE) / NM; ++st) {
                 if (st == 0) prob_max(si0, si1, 0, 8, mx);
@@ -451,25 +463,38 @@ __global__ void __launch_bounds__(256, 1) fp8_causal_fwd(Fp8Params a) {
         }
         pout = i32x8{pw[0], pw[1], pw[2], pw[3], pw[4], pw[5], pw[6], pw[7]};
     };
-    // Fully visible block j with every neighbour in range.
-    auto fast_iteration = [&](int j) {
+    // Fully visible block j (slot r = j%3, a compile-time constant) with every
+    // neighbour in range.  Phase 1 issues no operand reads, so the LDS staging work
+    // (V^T build, K and V stores) goes there.
+    auto fast_iteration = [&](int j, auto rc) {
+        constexpr int r = decltype(rc)::value;
+        constexpr int s0 = r, s1 = (r + 1) % 3, s2 = (r + 2) % 3;
         float Ma, Mb;
-        fast_phase(j, qb, sb0, sb1, j - 1, pb, sbb, ob, lb, sa0, sa1, Ma, pa, [&](int i) {
-            if (i == 0) transpose_read(j + 1);
-            if (i == NM / 2) transpose_write(j + 1);
+        fast_phase(false, 0, 0, qb, sb0, sb1, pb, sbb, ob, lb, sa0, sa1, Ma, pa, [&](int i) {
+            if (i == 0) transpose_read(s1);
+            if (i == 3) transpose_write(s1);
+            if (i == 4) lstore(s2);
+            if (i == 5) gload(j + 3);
         });
         commit(Ma, refa, oa, la, sba);
-        fast_phase(j + 1, qa, sa0, sa1, j, pa, sba, oa, la, sb0, sb1, Mb, pb, [&](int i) {
-            if (i == 1) lstore(j + 2);
-            if (i == 2) gload(j + 3);
-        });
+        fast_phase(true, s1, s0, qa, sa0, sa1, pa, sba, oa, la, sb0, sb1, Mb, pb, [&](int) {});
         commit(Mb, refb, ob, lb, sbb);
         block_sync();
     };
+
+    // Blocks [1, jfast) are fully visible to every wave of the workgroup and have all
+    // neighbours in range.
+    int jfast = max(1, min(nblk - 3, q0 / KB));
+    asm volatile("" : "+s"(jfast));   // opaque bound: keep the fast loop a loop of its own
     iteration(0);
-    for (int j = 1; j < jfast; ++j) fast_iteration(j);
-    for (int j = jfast; j < nblk; ++j) iteration(j);
-    pv(nblk - 1, pb, sbb, ob, lb);
+    int j = 1;
+    for (; j + 2 < jfast; j += 3) {
+        fast_iteration(j, std::integral_constant<int, 1>{});
+        fast_iteration(j + 1, std::integral_constant<int, 2>{});
+        fast_iteration(j + 2, std::integral_constant<int, 0>{});
+    }
+    for (; j < nblk; ++j) iteration(j);
+    pv(pb, sbb, ob, lb);   // op holds V^T(nblk-1)
     // The matrix instructions ignore EXEC: settling the accumulators here also keeps
     // all matrix work (and any operand copies it needs) out of the divergent stores.
     acc_settle(oa, la);

@@ -33,6 +33,17 @@ __device__ __forceinline__ i32x4 load16(const void* p) {
     return *reinterpret_cast<const i32x4*>(p);
 }
 
+// Raw buffer resource over [base, base + bytes): 16-byte loads at byte offsets at
+// or past `bytes` return zeros without touching memory.  Word 3 selects the
+// 32-bit data format of untyped gfx9-family buffer accesses.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, int bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, bytes, 0x00020000);
+}
+
+__device__ __forceinline__ i32x4 buffer_load16(__amdgpu_buffer_rsrc_t r, int offset) {
+    return __builtin_amdgcn_raw_buffer_load_b128(r, offset, 0, 0);
+}
+
 __device__ __forceinline__ i32x4 lds_load16(const ATTN_LDS uint8_t* p) {
     return *reinterpret_cast<const ATTN_LDS i32x4*>(p);
 }
