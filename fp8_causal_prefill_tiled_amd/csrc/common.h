@@ -86,6 +86,20 @@ __device__ __forceinline__ void mfma_f8_scaled_acc(f32x16& acc, const i32x8& a, 
         : "v"(a), "v"(b), "v"(scale_a), "v"(scale_b));
 }
 
+// The same with the accumulator in VGPRs, tied to the destination (the builtin in
+// VGPR form may give the result a register of its own and copy it back).
+__device__ __forceinline__ void mfma_f8_scaled_vacc(f32x16& acc, const i32x8& a, const i32x8& b, int scale_a,
+                                                    int scale_b) {
+    asm("v_mfma_scale_f32_32x32x64_f8f6f4 %0, %1, %2, %0, %3, %4 op_sel_hi:[0,0,0]"
+        : "+v"(acc)
+        : "v"(a), "v"(b), "v"(scale_a), "v"(scale_b));
+}
+
+// VGPR counterpart of acc_settle.
+__device__ __forceinline__ void vacc_settle(f32x16 (&o)[4], f32x16& l) {
+    asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+v"(o[0]), "+v"(o[1]), "+v"(o[2]), "+v"(o[3]), "+v"(l));
+}
+
 // Before any other instruction touches accumulators written by mfma_f8_scaled_acc:
 // a 16-pass MFMA needs independent cycles before its result may be read, which
 // the compiler does not insert for inline asm.  24 wait states cover the 16-pass
@@ -95,11 +109,13 @@ __device__ __forceinline__ void acc_settle(f32x16 (&o)[4], f32x16& l) {
     asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+a"(o[0]), "+a"(o[1]), "+a"(o[2]), "+a"(o[3]), "+a"(l));
 }
 
-// Fence the scheduler on both sides of a workgroup barrier: without it, ALU and
-// matrix instructions that do not touch memory may be moved across s_barrier.
+// Workgroup barrier for LDS producer/consumer hand-off: waits for this wave's LDS
+// operations only (outstanding global loads keep flowing across it), and fences
+// the scheduler on both sides (ALU and matrix instructions that do not touch
+// memory could otherwise be moved across s_barrier).
 __device__ __forceinline__ void block_sync() {
     __builtin_amdgcn_sched_barrier(0);
-    __syncthreads();
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
     __builtin_amdgcn_sched_barrier(0);
 }
 
