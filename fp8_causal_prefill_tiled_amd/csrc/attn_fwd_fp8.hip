@@ -163,9 +163,12 @@ __global__ void __launch_bounds__(512) fp8_causal_fwd(Fp8Params a) {
             so[i] = T::OFF_VS + row * 128 + 16 * (cc ^ v_swz(row));
         }
     }
+    // Every block index is loaded in order (blocks past the last one read zeros),
+    // so the compiler's wait before a store leaves the loads of the next block in
+    // flight.
     auto gload = [&](int j, auto setc) {
         constexpr int set = decltype(setc)::value;
-        const int rows = min(S - j * KB, KB);
+        const int rows = max(min(S - j * KB, KB), 0);   // blocks past the end load zeros, no traffic
         if (grp == 0) {
             const auto r = buffer_rsrc(kbase + (int64_t)j * KB * k_row, rows * k_row);
 #pragma unroll
@@ -354,12 +357,16 @@ __global__ void __launch_bounds__(512) fp8_causal_fwd(Fp8Params a) {
 
     // ---- prologue: K(0), K(1) and V(0), V(1) staged, blocks 2 and 3 in flight,
     // V^T(0) built, S^T(0) for every wave, P(0) for G0.
-    gload(0, std::integral_constant<int, 0>{});
-    if (nblk > 1) gload(1, std::integral_constant<int, 1>{});
-    lstore(0, std::integral_constant<int, 0>{});
-    if (nblk > 1) lstore(1, std::integral_constant<int, 1>{});
-    if (nblk > 2) gload(2, std::integral_constant<int, 0>{});
-    if (nblk > 3) gload(3, std::integral_constant<int, 1>{});
+    // Issue order keeps the rule lstore relies on: when block jb is stored, the
+    // loads of block jb+1 (if it exists) are the only ones issued after its own.
+    using I0 = std::integral_constant<int, 0>;
+    using I1 = std::integral_constant<int, 1>;
+    gload(0, I0{});
+    gload(1, I1{});
+    lstore(0, I0{});
+    gload(2, I0{});
+    lstore(1, I1{});
+    gload(3, I1{});
     block_sync();
     if (grp == 0) transpose_v(0);
     {
@@ -378,38 +385,37 @@ __global__ void __launch_bounds__(512) fp8_causal_fwd(Fp8Params a) {
     // ---- main loop.  Each group runs a loop of its own (one code path per loop
     // keeps the accumulators in fixed registers); both execute two barriers per
     // iteration.  Unrolled twice so the staging register set (j%2) is a constant.
+    // Nothing is guarded: staging past the last block moves zeros into free slots,
+    // a vector phase past it sees only masked keys (P = 0, no reference move), and
+    // the extra MFMA phase of an odd block count adds 0 * 0.
     if (grp == 0) {
         valu_phase(0);
         auto iteration = [&](int j, auto setc) {
             mfma_phase(j);                                // phase A
-            if (j + 2 < nblk) lstore(j + 2, setc);
-            if (j + 4 < nblk) gload(j + 4, setc);
-            if (j + 1 < nblk) transpose_v(j + 1);
+            lstore(j + 2, setc);
+            gload(j + 4, setc);
+            transpose_v(j + 1);
             block_sync();
-            if (j + 1 < nblk) valu_phase(j + 1);          // phase B
+            valu_phase(j + 1);                            // phase B
             block_sync();
         };
-        int j = 0;
-        for (; j + 1 < nblk; j += 2) {
-            iteration(j, std::integral_constant<int, 0>{});
-            iteration(j + 1, std::integral_constant<int, 1>{});
+        for (int j = 0; j < nblk; j += 2) {
+            iteration(j, I0{});
+            iteration(j + 1, I1{});
         }
-        if (j < nblk) iteration(j, std::integral_constant<int, 0>{});
     } else {
         auto iteration = [&](int j, auto setc) {
             valu_phase(j);                                // phase A
             block_sync();
             mfma_phase(j);                                // phase B
-            if (j + 2 < nblk) lstore(j + 2, setc);
-            if (j + 4 < nblk) gload(j + 4, setc);
+            lstore(j + 2, setc);
+            gload(j + 4, setc);
             block_sync();
         };
-        int j = 0;
-        for (; j + 1 < nblk; j += 2) {
-            iteration(j, std::integral_constant<int, 0>{});
-            iteration(j + 1, std::integral_constant<int, 1>{});
+        for (int j = 0; j < nblk; j += 2) {
+            iteration(j, I0{});
+            iteration(j + 1, I1{});
         }
-        if (j < nblk) iteration(j, std::integral_constant<int, 0>{});
     }
     // The matrix instructions ignore EXEC: settling the accumulators here also keeps
     // all matrix work (and any operand copies it needs) out of the divergent stores.

@@ -36,8 +36,14 @@ __device__ __forceinline__ i32x4 load16(const void* p) {
 // Raw buffer resource over [base, base + bytes): 16-byte loads at byte offsets at
 // or past `bytes` return zeros without touching memory.  Word 3 selects the
 // 32-bit data format of untyped gfx9-family buffer accesses.
+// The base and size must be wave-uniform; they are read from the first lane, so
+// the descriptor lives in SGPRs (no per-lane waterfall around the loads).
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, int bytes) {
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, bytes, 0x00020000);
+    const unsigned long long a = (unsigned long long)base;
+    const unsigned long long lo = (unsigned)__builtin_amdgcn_readfirstlane((int)a);
+    const unsigned long long hi = (unsigned)__builtin_amdgcn_readfirstlane((int)(a >> 32));
+    return __builtin_amdgcn_make_buffer_rsrc((void*)(lo | (hi << 32)), (short)0,
+                                             __builtin_amdgcn_readfirstlane(bytes), 0x00020000);
 }
 
 __device__ __forceinline__ i32x4 buffer_load16(__amdgpu_buffer_rsrc_t r, int offset) {
