@@ -78,12 +78,14 @@ __device__ __forceinline__ int v_swz(int row) { return (row & 3) | (((row >> 3) 
 // probability code.  A single wave issues roughly one vector instruction per
 // 5-6 cycles, so one wave alone cannot both keep a 64-cycle MFMA pipeline busy
 // and issue the ~100 vector instructions each 9-MFMA phase needs; two waves can.
-// The MFMA wave also does the block staging, which costs it little issue time:
-//     G0 in phase A: K block j+2 registers -> LDS, buffer loads of K block j+4,
-//                    V^T(j+1) built from the key-major V staging tile
-//     G1 in phase B: V block j+2 registers -> LDS staging, buffer loads of V block j+4
+// The MFMA wave also stages a block between its MFMAs, while the matrix pipe is
+// busy, and V^T is built by whichever wave of phase A has the shorter phase:
+//     phase A:  G0 K block j+2 registers -> LDS, buffer loads of K block j+3
+//               V^T(j+1) from the key-major V staging tile (G1 with Lean P,
+//               G0 with the exponential path)
+//     phase B:  G1 V block j+2 registers -> LDS staging, buffer loads of V block j+3
 // K, V^T and V staging tiles each have 2 LDS slots (block j in slot j%2); the
-// buffer loads run two iterations ahead into two register sets.  V^T row d holds
+// buffer loads run one iteration ahead of their LDS stores.  V^T row d holds
 // the block's 64 keys in the byte order of the probability operand, so both
 // matrix operands are plain 16-byte LDS reads; it is built once per workgroup
 // with the transposing ds_read_b64_tr_b8, far slower per byte than
@@ -145,10 +147,10 @@ __global__ void __launch_bounds__(512) fp8_causal_fwd(Fp8Params a) {
         }
     }
 
-    // ---- staging.  G0 moves K blocks, G1 V blocks: HBM -> registers (gload, set
-    // j%2, two iterations ahead) -> LDS (lstore).  Per-lane byte offsets of the
-    // staged chunks inside a block (global) and inside an LDS slot.
-    i32x4 st[2][SPT];
+    // ---- staging.  G0 moves K blocks, G1 V blocks: HBM -> registers (gload, one
+    // iteration ahead) -> LDS (lstore).  Per-lane byte offsets of the staged chunks
+    // inside a block (global) and inside an LDS slot.
+    i32x4 st[SPT];
     int go[SPT], so[SPT];
 #pragma unroll
     for (int i = 0; i < SPT; ++i) {
@@ -163,36 +165,33 @@ __global__ void __launch_bounds__(512) fp8_causal_fwd(Fp8Params a) {
             so[i] = T::OFF_VS + row * 128 + 16 * (cc ^ v_swz(row));
         }
     }
-    // Every block index is loaded in order (blocks past the last one read zeros),
-    // so the compiler's wait before a store leaves the loads of the next block in
-    // flight.
-    auto gload = [&](int j, auto setc) {
-        constexpr int set = decltype(setc)::value;
-        const int rows = max(min(S - j * KB, KB), 0);   // blocks past the end load zeros, no traffic
+    // Every block index is loaded (blocks past the last one read zeros through an
+    // empty range), so the staging steps need no guards.
+    auto gload = [&](int j) {
+        const int rows = max(min(S - j * KB, KB), 0);
         if (grp == 0) {
             const auto r = buffer_rsrc(kbase + (int64_t)j * KB * k_row, rows * k_row);
 #pragma unroll
-            for (int i = 0; i < KPT; ++i) st[set][i] = buffer_load16(r, go[i]);
+            for (int i = 0; i < KPT; ++i) st[i] = buffer_load16(r, go[i]);
         } else {
             const auto r = buffer_rsrc(vbase + (int64_t)j * KB * v_row, rows * v_row);
 #pragma unroll
-            for (int i = 0; i < VPT; ++i) st[set][i] = buffer_load16(r, go[i]);
+            for (int i = 0; i < VPT; ++i) st[i] = buffer_load16(r, go[i]);
         }
     };
-    auto lstore = [&](int j, auto setc) {   // G0: K slot j%2, G1: staging slot j%2
-        constexpr int set = decltype(setc)::value;
+    auto lstore = [&](int j) {   // G0: K slot j%2, G1: staging slot j%2
         if (grp == 0) {
             ATTN_LDS uint8_t* base = smem + (j & 1) * T::K_BYTES;
 #pragma unroll
-            for (int i = 0; i < KPT; ++i) lds_store16(base + so[i], st[set][i]);
+            for (int i = 0; i < KPT; ++i) lds_store16(base + so[i], st[i]);
         } else {
             ATTN_LDS uint8_t* base = smem + (j & 1) * T::V_BYTES;
 #pragma unroll
-            for (int i = 0; i < VPT; ++i) lds_store16(base + so[i], st[set][i]);
+            for (int i = 0; i < VPT; ++i) lds_store16(base + so[i], st[i]);
         }
     };
 
-    // ---- V^T construction by G0: V^T row d holds the 64 keys at positions
+    // ---- V^T construction: V^T row d holds the 64 keys at positions
     // p = 32h + t in the probability-byte order key(h, t) = 32(t/16) + 8((t%16)/4)
     // + 4h + t%4.  16-lane group Gi (of 32) builds the chunk d in [16(Gi%8), +16),
     // p in [16(Gi/8), +16) from two transposing reads of 8 keys (rows) x 16 d
@@ -212,17 +211,26 @@ __global__ void __launch_bounds__(512) fp8_causal_fwd(Fp8Params a) {
         }
         tr_dst[u] = T::OFF_VT + (dbase + n) * T::VT_STRIDE + p0;
     }
-    auto transpose_v = [&](int j) {   // staging slot j%2 -> V^T slot j%2
+    // Split in two so the transposing reads can be issued early and their latency
+    // hidden behind other work before the stores.
+    i32x2 tlo[TPT], thi[TPT];
+    auto transpose_read = [&](int j) {   // staging slot j%2 -> registers
         const ATTN_LDS uint8_t* src = smem + (j & 1) * T::V_BYTES;
-        ATTN_LDS uint8_t* dst = smem + (j & 1) * T::VT_BYTES;
-        i32x2 lo[TPT], hi[TPT];
 #pragma unroll
         for (int u = 0; u < TPT; ++u) {
-            lo[u] = lds_read_tr8(src + tr_off[u][0]);
-            hi[u] = lds_read_tr8(src + tr_off[u][1]);
+            tlo[u] = lds_read_tr8(src + tr_off[u][0]);
+            thi[u] = lds_read_tr8(src + tr_off[u][1]);
         }
+    };
+    auto transpose_write = [&](int j) {   // registers -> V^T slot j%2
+        ATTN_LDS uint8_t* dst = smem + (j & 1) * T::VT_BYTES;
 #pragma unroll
-        for (int u = 0; u < TPT; ++u) lds_store16(dst + tr_dst[u], i32x4{lo[u][0], lo[u][1], hi[u][0], hi[u][1]});
+        for (int u = 0; u < TPT; ++u)
+            lds_store16(dst + tr_dst[u], i32x4{tlo[u][0], tlo[u][1], thi[u][0], thi[u][1]});
+    };
+    auto transpose_v = [&](int j) {
+        transpose_read(j);
+        transpose_write(j);
     };
 
     f32x16 o[4];
@@ -259,7 +267,9 @@ __global__ void __launch_bounds__(512) fp8_causal_fwd(Fp8Params a) {
     constexpr int NS = 2 * T::NKK;      // score MFMAs per block
     // Issue order: operand i (i < NS: K operand, key half i%2, d step i/2; else V^T
     // rows 32(i-NS)) is read two MFMAs ahead of its use.
-    auto mfma_phase = [&](int j) {
+    // extra(i) runs after MFMA i: the staging work of the MFMA wave, issued while the
+    // matrix pipe is busy.
+    auto mfma_phase = [&](int j, auto&& extra) {
         __builtin_amdgcn_s_setprio(1);   // matrix issue wins arbitration against the partner wave
         const ATTN_LDS uint8_t* kp = smem + ((j + 1) & 1) * T::K_BYTES + c * T::K_STRIDE + 32 * hh;
         const ATTN_LDS uint8_t* vp = smem + T::OFF_VT + (j & 1) * T::VT_BYTES + c * T::VT_STRIDE + 32 * hh;
@@ -284,6 +294,7 @@ __global__ void __launch_bounds__(512) fp8_causal_fwd(Fp8Params a) {
             } else {
                 mfma_f8_scaled_vacc(o[i - NS], opb[i % 3], pv_bytes, sa, sb);
             }
+            extra(i);
             __builtin_amdgcn_sched_barrier(0);
         }
         mfma_f8_scaled_vacc(lsum, ones, pv_bytes, sa, sb);
@@ -359,14 +370,11 @@ __global__ void __launch_bounds__(512) fp8_causal_fwd(Fp8Params a) {
     // V^T(0) built, S^T(0) for every wave, P(0) for G0.
     // Issue order keeps the rule lstore relies on: when block jb is stored, the
     // loads of block jb+1 (if it exists) are the only ones issued after its own.
-    using I0 = std::integral_constant<int, 0>;
-    using I1 = std::integral_constant<int, 1>;
-    gload(0, I0{});
-    gload(1, I1{});
-    lstore(0, I0{});
-    gload(2, I0{});
-    lstore(1, I1{});
-    gload(3, I1{});
+    gload(0);
+    lstore(0);
+    gload(1);
+    lstore(1);
+    gload(2);
     block_sync();
     if (grp == 0) transpose_v(0);
     {
@@ -384,37 +392,40 @@ __global__ void __launch_bounds__(512) fp8_causal_fwd(Fp8Params a) {
 
     // ---- main loop.  Each group runs a loop of its own (one code path per loop
     // keeps the accumulators in fixed registers); both execute two barriers per
-    // iteration.  Unrolled twice so the staging register set (j%2) is a constant.
-    // Nothing is guarded: staging past the last block moves zeros into free slots,
-    // a vector phase past it sees only masked keys (P = 0, no reference move), and
-    // the extra MFMA phase of an odd block count adds 0 * 0.
+    // iteration.  Nothing is guarded: staging past the last block moves zeros into
+    // free slots, a vector phase past it sees only masked keys (P = 0, no reference
+    // move), and an MFMA phase past it adds 0 * 0.
+    // The V^T build goes to the wave with the shorter phase A: the vector wave (G1)
+    // with Lean P, the matrix wave (G0) with the exponential path, whose vector
+    // phase is the longer one.
+    constexpr bool kTransposeOnMfma = PMODE == 0;
     if (grp == 0) {
         valu_phase(0);
-        auto iteration = [&](int j, auto setc) {
-            mfma_phase(j);                                // phase A
-            lstore(j + 2, setc);
-            gload(j + 4, setc);
-            transpose_v(j + 1);
+        for (int j = 0; j < nblk; ++j) {
+            mfma_phase(j, [&](int i) {                    // phase A
+                if (kTransposeOnMfma && i == 0) transpose_read(j + 1);
+                if (i == 1) lstore(j + 2);
+                if (i == 2) gload(j + 3);
+                if (kTransposeOnMfma && i == 4) transpose_write(j + 1);
+            });
             block_sync();
             valu_phase(j + 1);                            // phase B
             block_sync();
-        };
-        for (int j = 0; j < nblk; j += 2) {
-            iteration(j, I0{});
-            iteration(j + 1, I1{});
         }
     } else {
-        auto iteration = [&](int j, auto setc) {
-            valu_phase(j);                                // phase A
+        for (int j = 0; j < nblk; ++j) {
+            if (!kTransposeOnMfma) {                      // phase A
+                transpose_read(j + 1);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+            valu_phase(j);
+            if (!kTransposeOnMfma) transpose_write(j + 1);
             block_sync();
-            mfma_phase(j);                                // phase B
-            lstore(j + 2, setc);
-            gload(j + 4, setc);
+            mfma_phase(j, [&](int i) {                    // phase B
+                if (i == 1) lstore(j + 2);
+                if (i == 2) gload(j + 3);
+            });
             block_sync();
-        };
-        for (int j = 0; j < nblk; j += 2) {
-            iteration(j, I0{});
-            iteration(j + 1, I1{});
         }
     }
     // The matrix instructions ignore EXEC: settling the accumulators here also keeps
