@@ -70,8 +70,10 @@ __device__ __forceinline__ int v_swz(int row) { return (row & 3) | (((row >> 3) 
 // MarkTechPost).  A workgroup of 8 waves covers 256 query rows of one head;
 // waves w and w+4 share a SIMD and form the two groups G0 (waves 0-3) and G1
 // (waves 4-7).  Each iteration j is two phases separated by a workgroup barrier:
-//     phase A:  G0  MFMA(j): S^T(j+1) = K(j+1).Q^T, O^T += V^T(j).P(j)^T, L += 1.P(j)^T
-//               G1  VALU(j): mask, row max, block exponent, P(j) bytes, reference update
+//     phase A:  G0  MFMA(j): S^T(j+1) = K(j+1).Q^T, O^T += V^T(j).P(j)^T, L += 1.P(j)^T,
+//                   and in the shadow of the P.V MFMAs the mask, row max and block
+//                   exponent of block j+1
+//               G1  VALU(j): P(j) bytes, reference update
 //     phase B:  G0  VALU(j+1)
 //               G1  MFMA(j)
 // so on every SIMD one wave feeds the matrix core while its partner runs the
@@ -264,6 +266,89 @@ __global__ void __launch_bounds__(512) fp8_causal_fwd(Fp8Params a) {
     f32x16 s0, s1;              // S^T of the next block: keys [0,32) and [32,64)
     i32x8 pv_bytes;             // P(j), the B operand of the P.V MFMAs
     int sb = 127;               // its E8M0 scale byte
+    // ---- probabilities of block j in two parts.  prep: mask (diagonal blocks),
+    // block exponent M, the bias of the byte formula and the reference update
+    // decision; it runs on the MFMA wave right after the score MFMAs, in the shadow
+    // of the P.V MFMAs.  finish: P bytes, the rare exact rescale of O and L when the
+    // power-of-two reference moves (by more than kRefSlack), E8M0 scale byte; it is
+    // the vector phase.
+    float bias_n = 0.0f, nref_n = 0.0f;
+    bool need_n = false;
+    int sb_n = 127;
+    auto prep_mask = [&](int j) {
+        if (j >= jdiag) {
+            // key kb0 + off(r) + 4hh is visible iff off(r) <= min(qabs, S-1) - kb0 - 4hh
+            const int lim = min(qabs, S - 1) - j * KB - 4 * hh;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int off = 8 * (r >> 2) + (r & 3);
+                s0[r] = off <= lim ? s0[r] : -INFINITY;
+                s1[r] = off + 32 <= lim ? s1[r] : -INFINITY;
+            }
+        }
+    };
+    float mx_n = -INFINITY;
+    auto prep_max = [&](int r0, int r1) {
+        if (r0 == 0) mx_n = -INFINITY;
+#pragma unroll
+        for (int r = r0; r < r1; ++r) mx_n = fmaxf(fmaxf(mx_n, s0[r]), s1[r]);
+    };
+    auto prep_exponent = [&]() {
+        const float mx = fmaxf(mx_n, other_half(mx_n));
+        const float M = fmaxf(ceilf(mx * a.c), -1.0e30f);  // floor: rows with no visible key here
+        bias_n = PMODE == 0 ? 8.0f - M : 120.0f - 8.0f * M;
+        need_n = M > ref + kRefSlack;
+        nref_n = need_n ? M : ref;
+        sb_n = (int)fminf(fmaxf(M - 8.0f - nref_n, -127.0f), 127.0f) + 127;
+    };
+    auto prep = [&](int j) {
+        prep_mask(j);
+        prep_max(0, 16);
+        prep_exponent();
+    };
+    auto finish = [&]() {
+        int pw[8];
+        if (PMODE == 0) {
+#pragma unroll
+            for (int q4 = 0; q4 < 8; ++q4) {
+                const f32x16& x = q4 < 4 ? s0 : s1;
+                const int e = 4 * (q4 & 3);
+                const float p0 = __builtin_amdgcn_exp2f(fmaf(x[e + 0], a.c, bias_n));
+                const float p1 = __builtin_amdgcn_exp2f(fmaf(x[e + 1], a.c, bias_n));
+                const float p2 = __builtin_amdgcn_exp2f(fmaf(x[e + 2], a.c, bias_n));
+                const float p3 = __builtin_amdgcn_exp2f(fmaf(x[e + 3], a.c, bias_n));
+                const int wd = __builtin_amdgcn_cvt_pk_fp8_f32(p0, p1, 0, false);
+                pw[q4] = __builtin_amdgcn_cvt_pk_fp8_f32(p2, p3, wd, true);
+            }
+        } else {
+#pragma unroll
+            for (int q4 = 0; q4 < 8; ++q4) {
+                const f32x16& x = q4 < 4 ? s0 : s1;
+                const int e = 4 * (q4 & 3);
+                unsigned wd = 0;
+                wd = __builtin_amdgcn_cvt_pk_u8_f32(fmaf(x[e + 0], a.a8, bias_n), 0, wd);
+                wd = __builtin_amdgcn_cvt_pk_u8_f32(fmaf(x[e + 1], a.a8, bias_n), 1, wd);
+                wd = __builtin_amdgcn_cvt_pk_u8_f32(fmaf(x[e + 2], a.a8, bias_n), 2, wd);
+                wd = __builtin_amdgcn_cvt_pk_u8_f32(fmaf(x[e + 3], a.a8, bias_n), 3, wd);
+                pw[q4] = (int)wd;
+            }
+        }
+        pv_bytes = i32x8{pw[0], pw[1], pw[2], pw[3], pw[4], pw[5], pw[6], pw[7]};
+        if (__ballot(need_n)) {
+            vacc_settle(o, lsum);
+            const float f = __builtin_amdgcn_exp2f(ref - nref_n);   // exactly 1 for rows that do not move
+#pragma unroll
+            for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) o[dt][r] *= f;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) lsum[r] *= f;
+            vacc_settle(o, lsum);   // the rescaled values are back before the next MFMA reads them
+        }
+        ref = nref_n;
+        sb = sb_n;
+    };
+
     constexpr int NS = 2 * T::NKK;      // score MFMAs per block
     // Issue order: operand i (i < NS: K operand, key half i%2, d step i/2; else V^T
     // rows 32(i-NS)) is read two MFMAs ahead of its use.
@@ -294,76 +379,16 @@ __global__ void __launch_bounds__(512) fp8_causal_fwd(Fp8Params a) {
             } else {
                 mfma_f8_scaled_vacc(o[i - NS], opb[i % 3], pv_bytes, sa, sb);
             }
+            // prep of block j+1 once its score MFMAs have completed
+            if (i == NS + 1) prep_mask(j + 1);
+            if (i == NS + 2) prep_max(0, 8);
+            if (i == NS + 3) prep_max(8, 16);
             extra(i);
             __builtin_amdgcn_sched_barrier(0);
         }
         mfma_f8_scaled_vacc(lsum, ones, pv_bytes, sa, sb);
+        prep_exponent();
         __builtin_amdgcn_s_setprio(0);
-    };
-
-    // ---- VALU phase of block j: mask (diagonal blocks), block exponent M, P bytes,
-    // lazy power-of-two reference (moves, with an exact rescale of O and L, only
-    // when M exceeds it by more than kRefSlack), E8M0 scale byte.
-    auto valu_phase = [&](int j) {
-        if (j >= jdiag) {
-            // key kb0 + off(r) + 4hh is visible iff off(r) <= min(qabs, S-1) - kb0 - 4hh
-            const int lim = min(qabs, S - 1) - j * KB - 4 * hh;
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int off = 8 * (r >> 2) + (r & 3);
-                s0[r] = off <= lim ? s0[r] : -INFINITY;
-                s1[r] = off + 32 <= lim ? s1[r] : -INFINITY;
-            }
-        }
-        float mx = -INFINITY;
-#pragma unroll
-        for (int r = 0; r < 16; ++r) mx = fmaxf(fmaxf(mx, s0[r]), s1[r]);
-        mx = fmaxf(mx, other_half(mx));
-        const float M = fmaxf(ceilf(mx * a.c), -1.0e30f);  // floor: rows with no visible key here
-        int pw[8];
-        if (PMODE == 0) {
-            const float bias = 8.0f - M;
-#pragma unroll
-            for (int q4 = 0; q4 < 8; ++q4) {
-                const f32x16& x = q4 < 4 ? s0 : s1;
-                const int e = 4 * (q4 & 3);
-                const float p0 = __builtin_amdgcn_exp2f(fmaf(x[e + 0], a.c, bias));
-                const float p1 = __builtin_amdgcn_exp2f(fmaf(x[e + 1], a.c, bias));
-                const float p2 = __builtin_amdgcn_exp2f(fmaf(x[e + 2], a.c, bias));
-                const float p3 = __builtin_amdgcn_exp2f(fmaf(x[e + 3], a.c, bias));
-                const int wd = __builtin_amdgcn_cvt_pk_fp8_f32(p0, p1, 0, false);
-                pw[q4] = __builtin_amdgcn_cvt_pk_fp8_f32(p2, p3, wd, true);
-            }
-        } else {
-            const float bias = 120.0f - 8.0f * M;
-#pragma unroll
-            for (int q4 = 0; q4 < 8; ++q4) {
-                const f32x16& x = q4 < 4 ? s0 : s1;
-                const int e = 4 * (q4 & 3);
-                unsigned wd = 0;
-                wd = __builtin_amdgcn_cvt_pk_u8_f32(fmaf(x[e + 0], a.a8, bias), 0, wd);
-                wd = __builtin_amdgcn_cvt_pk_u8_f32(fmaf(x[e + 1], a.a8, bias), 1, wd);
-                wd = __builtin_amdgcn_cvt_pk_u8_f32(fmaf(x[e + 2], a.a8, bias), 2, wd);
-                wd = __builtin_amdgcn_cvt_pk_u8_f32(fmaf(x[e + 3], a.a8, bias), 3, wd);
-                pw[q4] = (int)wd;
-            }
-        }
-        pv_bytes = i32x8{pw[0], pw[1], pw[2], pw[3], pw[4], pw[5], pw[6], pw[7]};
-        const bool need = M > ref + kRefSlack;
-        const float nref = need ? M : ref;
-        if (__ballot(need)) {
-            vacc_settle(o, lsum);
-            const float f = __builtin_amdgcn_exp2f(ref - nref);   // exactly 1 for rows that do not move
-#pragma unroll
-            for (int dt = 0; dt < 4; ++dt)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) o[dt][r] *= f;
-#pragma unroll
-            for (int r = 0; r < 16; ++r) lsum[r] *= f;
-            vacc_settle(o, lsum);   // the rescaled values are back before the next MFMA reads them
-        }
-        ref = nref;
-        sb = (int)fminf(fmaxf(M - 8.0f - ref, -127.0f), 127.0f) + 127;
     };
 
     // ---- prologue: K(0), K(1) and V(0), V(1) staged, blocks 2 and 3 in flight,
@@ -399,8 +424,9 @@ __global__ void __launch_bounds__(512) fp8_causal_fwd(Fp8Params a) {
     // with Lean P, the matrix wave (G0) with the exponential path, whose vector
     // phase is the longer one.
     constexpr bool kTransposeOnMfma = PMODE == 0;
+    prep(0);
     if (grp == 0) {
-        valu_phase(0);
+        finish();
         for (int j = 0; j < nblk; ++j) {
             mfma_phase(j, [&](int i) {                    // phase A
                 if (kTransposeOnMfma && i == 0) transpose_read(j + 1);
@@ -409,7 +435,7 @@ __global__ void __launch_bounds__(512) fp8_causal_fwd(Fp8Params a) {
                 if (kTransposeOnMfma && i == 4) transpose_write(j + 1);
             });
             block_sync();
-            valu_phase(j + 1);                            // phase B
+            finish();                                     // phase B
             block_sync();
         }
     } else {
@@ -418,7 +444,7 @@ __global__ void __launch_bounds__(512) fp8_causal_fwd(Fp8Params a) {
                 transpose_read(j + 1);
                 __builtin_amdgcn_sched_barrier(0);
             }
-            valu_phase(j);
+            finish();
             if (!kTransposeOnMfma) transpose_write(j + 1);
             block_sync();
             mfma_phase(j, [&](int i) {                    // phase B
