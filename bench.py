@@ -28,7 +28,7 @@ def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="gauss32k")
     ap.add_argument("--mode", default="lean", choices=["lean", "exact"])
     ap.add_argument("--dtype", default="fp8", choices=["fp8", "bf16"])
@@ -98,15 +98,16 @@ def cpu_baseline(w, d, out_gpu, seconds, dtype):
     """Time the CPU oracle (fp64 attention) on a bounded sample of the same workload and
     compare the GPU output on those rows.  Returns the cpu_baseline object.
 
-    Sample: query rows spread over 0..S-1 (longest causal prefixes first), in chunks of 64,
-    for three heads, until about `seconds` of oracle time has been spent."""
+    Sample: query rows spread over 0..S-1 (every 64th row, longest causal prefixes first, then
+    the next residue), in chunks of 64, for three heads, until about `seconds` of oracle time
+    has been spent."""
     import numpy as np
     from threadpoolctl import threadpool_info
     from oracle.attention64 import attention_fp64, dequantize
 
     threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
     S = w.S
-    order = np.linspace(S - 1, 0, 4096).astype(np.int64)
+    order = np.arange(S - 1, -1, -1, dtype=np.int64)[np.argsort(np.arange(S) % 64, kind="stable")]
     heads = [0, w.Hq // 2, w.Hq - 1]
     per_head = []
     for h in heads:
