@@ -69,28 +69,31 @@ __device__ __forceinline__ int v_swz(int row) { return (row & 3) | (((row >> 3) 
 // Two-wave ping-pong ("Two-wave ping-pong schedule", Zyphra ZYFA page,
 // MarkTechPost).  A workgroup of 8 waves covers 256 query rows of one head;
 // waves w and w+4 share a SIMD and form the two groups G0 (waves 0-3) and G1
-// (waves 4-7).  Each iteration j is two phases separated by a workgroup barrier:
-//     phase A:  G0  MFMA(j): S^T(j+1) = K(j+1).Q^T, O^T += V^T(j).P(j)^T, L += 1.P(j)^T,
-//                   and in the shadow of the P.V MFMAs the mask, row max and block
-//                   exponent of block j+1
-//               G1  VALU(j): P(j) bytes, reference update
-//     phase B:  G0  VALU(j+1)
-//               G1  MFMA(j)
-// so on every SIMD one wave feeds the matrix core while its partner runs the
-// probability code.  A single wave issues roughly one vector instruction per
-// 5-6 cycles, so one wave alone cannot both keep a 64-cycle MFMA pipeline busy
-// and issue the ~100 vector instructions each 9-MFMA phase needs; two waves can.
+// (waves 4-7).  In iteration j the two groups run their phases in opposite
+// order:
+//     G0:  MFMA(j), then VALU(j+1)
+//     G1:  VALU(j), then MFMA(j)
+// MFMA(j): S^T(j+1) = K(j+1).Q^T, O^T += V^T(j).P(j)^T, L += 1.P(j)^T, and in the
+// shadow of the P.V MFMAs the mask, row max and block exponent of block j+1.
+// VALU(j): P(j) bytes and the reference update.  One workgroup barrier ends the
+// iteration; starting from it, on every SIMD one wave feeds the matrix core while
+// its partner runs the probability code, and the order is restored at every
+// barrier.  A single wave issues roughly one vector instruction per 5-6 cycles,
+// so one wave alone cannot both keep a 64-cycle MFMA pipeline busy and issue the
+// ~100 vector instructions each 9-MFMA phase needs; two waves can.
 // The MFMA wave also stages a block between its MFMAs, while the matrix pipe is
-// busy, and V^T is built by whichever wave of phase A has the shorter phase:
-//     phase A:  G0 K block j+2 registers -> LDS, buffer loads of K block j+3
-//               V^T(j+1) from the key-major V staging tile (G1 with Lean P,
-//               G0 with the exponential path)
-//     phase B:  G1 V block j+2 registers -> LDS staging, buffer loads of V block j+3
+// busy, and V^T is built by whichever wave runs its vector phase first when
+// that phase is the shorter one:
+//     G0 (MFMA(j)):  K block j+2 registers -> LDS, buffer loads of K block j+3;
+//                    V^T(j+1) with the exponential path
+//     G1 (VALU(j)):  V^T(j+1) with Lean P
+//     G1 (MFMA(j)):  V block j+2 registers -> LDS staging, buffer loads of V block j+3
 // K, V^T and V staging tiles each have 2 LDS slots (block j in slot j%2); the
-// buffer loads run one iteration ahead of their LDS stores.  V^T row d holds
-// the block's 64 keys in the byte order of the probability operand, so both
-// matrix operands are plain 16-byte LDS reads; it is built once per workgroup
-// with the transposing ds_read_b64_tr_b8, far slower per byte than
+// buffer loads run one iteration ahead of their LDS stores, and every LDS
+// producer/consumer pair is separated by the end-of-iteration barrier.  V^T row
+// d holds the block's 64 keys in the byte order of the probability operand, so
+// both matrix operands are plain 16-byte LDS reads; it is built once per
+// workgroup with the transposing ds_read_b64_tr_b8, far slower per byte than
 // ds_read_b128 on gfx950.  Buffer loads use a range ending at row S, so rows
 // past S read as zeros.
 template <int DQK, int PMODE>
@@ -416,7 +419,7 @@ __global__ void __launch_bounds__(512) fp8_causal_fwd(Fp8Params a) {
     block_sync();
 
     // ---- main loop.  Each group runs a loop of its own (one code path per loop
-    // keeps the accumulators in fixed registers); both execute two barriers per
+    // keeps the accumulators in fixed registers); both execute one barrier per
     // iteration.  Nothing is guarded: staging past the last block moves zeros into
     // free slots, a vector phase past it sees only masked keys (P = 0, no reference
     // move), and an MFMA phase past it adds 0 * 0.
@@ -428,26 +431,24 @@ __global__ void __launch_bounds__(512) fp8_causal_fwd(Fp8Params a) {
     if (grp == 0) {
         finish();
         for (int j = 0; j < nblk; ++j) {
-            mfma_phase(j, [&](int i) {                    // phase A
+            mfma_phase(j, [&](int i) {                    // MFMA(j)
                 if (kTransposeOnMfma && i == 0) transpose_read(j + 1);
                 if (i == 1) lstore(j + 2);
                 if (i == 2) gload(j + 3);
                 if (kTransposeOnMfma && i == 4) transpose_write(j + 1);
             });
-            block_sync();
-            finish();                                     // phase B
+            finish();                                     // VALU(j+1)
             block_sync();
         }
     } else {
         for (int j = 0; j < nblk; ++j) {
-            if (!kTransposeOnMfma) {                      // phase A
+            if (!kTransposeOnMfma) {                      // VALU(j)
                 transpose_read(j + 1);
                 __builtin_amdgcn_sched_barrier(0);
             }
             finish();
             if (!kTransposeOnMfma) transpose_write(j + 1);
-            block_sync();
-            mfma_phase(j, [&](int i) {                    // phase B
+            mfma_phase(j, [&](int i) {                    // MFMA(j)
                 if (i == 1) lstore(j + 2);
                 if (i == 2) gload(j + 3);
             });
