@@ -81,13 +81,12 @@ __device__ __forceinline__ int v_swz(int row) { return (row & 3) | (((row >> 3) 
 // barrier.  A single wave issues roughly one vector instruction per 5-6 cycles,
 // so one wave alone cannot both keep a 64-cycle MFMA pipeline busy and issue the
 // ~100 vector instructions each 9-MFMA phase needs; two waves can.
-// The MFMA wave also stages a block between its MFMAs, while the matrix pipe is
-// busy, and V^T is built by whichever wave runs its vector phase first when
-// that phase is the shorter one:
+// The MFMA wave also does the block staging between its MFMAs, while the matrix
+// pipe is busy:
 //     G0 (MFMA(j)):  K block j+2 registers -> LDS, buffer loads of K block j+3;
 //                    V^T(j+1) with the exponential path
-//     G1 (VALU(j)):  V^T(j+1) with Lean P
-//     G1 (MFMA(j)):  V block j+2 registers -> LDS staging, buffer loads of V block j+3
+//     G1 (MFMA(j)):  V block j+2 registers -> LDS staging, buffer loads of V block j+3;
+//                    V^T(j+1) with Lean P
 // K, V^T and V staging tiles each have 2 LDS slots (block j in slot j%2); the
 // buffer loads run one iteration ahead of their LDS stores, and every LDS
 // producer/consumer pair is separated by the end-of-iteration barrier.  V^T row
@@ -423,34 +422,30 @@ __global__ void __launch_bounds__(512) fp8_causal_fwd(Fp8Params a) {
     // iteration.  Nothing is guarded: staging past the last block moves zeros into
     // free slots, a vector phase past it sees only masked keys (P = 0, no reference
     // move), and an MFMA phase past it adds 0 * 0.
-    // The V^T build goes to the wave with the shorter phase A: the vector wave (G1)
-    // with Lean P, the matrix wave (G0) with the exponential path, whose vector
-    // phase is the longer one.
-    constexpr bool kTransposeOnMfma = PMODE == 0;
+    // V^T is built inside an MFMA phase, between MFMAs: by G1 with Lean P (G1's
+    // iteration is otherwise the shorter one), by G0 with the exponential path.
+    constexpr bool kTransposeOnG0 = PMODE == 0;
     prep(0);
     if (grp == 0) {
         finish();
         for (int j = 0; j < nblk; ++j) {
             mfma_phase(j, [&](int i) {                    // MFMA(j)
-                if (kTransposeOnMfma && i == 0) transpose_read(j + 1);
+                if (kTransposeOnG0 && i == 0) transpose_read(j + 1);
                 if (i == 1) lstore(j + 2);
                 if (i == 2) gload(j + 3);
-                if (kTransposeOnMfma && i == 4) transpose_write(j + 1);
+                if (kTransposeOnG0 && i == 4) transpose_write(j + 1);
             });
             finish();                                     // VALU(j+1)
             block_sync();
         }
     } else {
         for (int j = 0; j < nblk; ++j) {
-            if (!kTransposeOnMfma) {                      // VALU(j)
-                transpose_read(j + 1);
-                __builtin_amdgcn_sched_barrier(0);
-            }
-            finish();
-            if (!kTransposeOnMfma) transpose_write(j + 1);
+            finish();                                     // VALU(j)
             mfma_phase(j, [&](int i) {                    // MFMA(j)
+                if (!kTransposeOnG0 && i == 0) transpose_read(j + 1);
                 if (i == 1) lstore(j + 2);
                 if (i == 2) gload(j + 3);
+                if (!kTransposeOnG0 && i == 4) transpose_write(j + 1);
             });
             block_sync();
         }
