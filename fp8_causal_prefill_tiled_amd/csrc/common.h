@@ -17,8 +17,6 @@ typedef short i16x8 __attribute__((ext_vector_type(8)));
 
 #define ATTN_LDS __attribute__((address_space(3)))
 
-constexpr float kLog2e = 1.4426950408889634f;
-
 // Value of lane (l ^ 32) - the other half of the wave.  v_permlane32_swap
 // exchanges the upper 32 lanes of its first operand with the lower 32 lanes of
 // its second; with both operands equal, lanes < 32 find their partner's value
@@ -75,25 +73,10 @@ __device__ __forceinline__ i16x8 i16x8_cat(i16x4 a, i16x4 b) {
     return i16x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
 }
 
-// Force accumulators to be materialised at this point in uniform control flow
-// (an empty asm that reads and writes them cannot be moved or sunk into a branch).
-__device__ __forceinline__ void pin_all(f32x16 (&o)[4], f32x16& l) {
-    asm volatile("" : "+v"(o[0]), "+v"(o[1]), "+v"(o[2]), "+v"(o[3]), "+v"(l));
-}
-
 // acc += A . B on the FP8 matrix cores (32x32x64, e4m3 operands) with per-lane E8M0
-// scales: A's byte from scale_a, B's from scale_b.  The accumulator lives in the
-// accumulation (AGPR) half of the register file, so score tiles computed by
-// compiler-generated MFMAs can take VGPRs that vector code reads directly.
-__device__ __forceinline__ void mfma_f8_scaled_acc(f32x16& acc, const i32x8& a, const i32x8& b, int scale_a,
-                                                   int scale_b) {
-    asm("v_mfma_scale_f32_32x32x64_f8f6f4 %0, %1, %2, %0, %3, %4 op_sel_hi:[0,0,0]"
-        : "+a"(acc)
-        : "v"(a), "v"(b), "v"(scale_a), "v"(scale_b));
-}
-
-// The same with the accumulator in VGPRs, tied to the destination (the builtin in
-// VGPR form may give the result a register of its own and copy it back).
+// scales: A's byte from scale_a, B's from scale_b.  The accumulator is tied to the
+// destination registers (the builtin in VGPR form may give the result registers of
+// its own and copy it back on every iteration).
 __device__ __forceinline__ void mfma_f8_scaled_vacc(f32x16& acc, const i32x8& a, const i32x8& b, int scale_a,
                                                     int scale_b) {
     asm("v_mfma_scale_f32_32x32x64_f8f6f4 %0, %1, %2, %0, %3, %4 op_sel_hi:[0,0,0]"
@@ -101,18 +84,13 @@ __device__ __forceinline__ void mfma_f8_scaled_vacc(f32x16& acc, const i32x8& a,
         : "v"(a), "v"(b), "v"(scale_a), "v"(scale_b));
 }
 
-// VGPR counterpart of acc_settle.
+// Before any other instruction touches accumulators written by mfma_f8_scaled_vacc:
+// a 16-pass MFMA needs independent cycles before its result may be read, which the
+// compiler does not insert for inline asm; 24 wait states cover it.  Being volatile
+// and tied to every accumulator, this also keeps all of those MFMAs in uniform
+// control flow ahead of it.
 __device__ __forceinline__ void vacc_settle(f32x16 (&o)[4], f32x16& l) {
     asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+v"(o[0]), "+v"(o[1]), "+v"(o[2]), "+v"(o[3]), "+v"(l));
-}
-
-// Before any other instruction touches accumulators written by mfma_f8_scaled_acc:
-// a 16-pass MFMA needs independent cycles before its result may be read, which
-// the compiler does not insert for inline asm.  24 wait states cover the 16-pass
-// XDL-write-to-read requirement.  Being volatile and tied to every accumulator,
-// this also keeps all of those MFMAs in uniform control flow ahead of it.
-__device__ __forceinline__ void acc_settle(f32x16 (&o)[4], f32x16& l) {
-    asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+a"(o[0]), "+a"(o[1]), "+a"(o[2]), "+a"(o[3]), "+a"(l));
 }
 
 // Workgroup barrier for LDS producer/consumer hand-off: waits for this wave's LDS
