@@ -43,9 +43,9 @@ def kernel_flags(src):
     # isfinite() tests must see NaN): inputs are finite by contract, so fmaxf
     # lowers to bare v_max3_f32 without NaN quieting.
     flags = ["-fno-honor-nans"] if src.endswith(".hip") else []
-    if src == "attn_fwd_fp8.hip":
-        # score MFMAs write VGPRs (read directly by the softmax code); the P.V
-        # accumulators are pinned to AGPRs by their inline-asm MFMA
+    if src in ("attn_fwd_fp8.hip", "attn_fwd_bf16.hip"):
+        # all matrix results in VGPRs: the score MFMAs' are read directly by the
+        # probability code, and the P.V accumulators' inline-asm MFMA ties them there
         flags += ["-mllvm", "-amdgpu-mfma-vgpr-form"]
     return flags
 

@@ -92,6 +92,9 @@ __device__ __forceinline__ void mfma_f8_scaled_vacc(f32x16& acc, const i32x8& a,
 __device__ __forceinline__ void vacc_settle(f32x16 (&o)[4], f32x16& l) {
     asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+v"(o[0]), "+v"(o[1]), "+v"(o[2]), "+v"(o[3]), "+v"(l));
 }
+__device__ __forceinline__ void vacc_settle(f32x16 (&o)[4]) {
+    asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+v"(o[0]), "+v"(o[1]), "+v"(o[2]), "+v"(o[3]));
+}
 
 // Workgroup barrier for LDS producer/consumer hand-off: waits for this wave's LDS
 // operations only (outstanding global loads keep flowing across it), and fences
