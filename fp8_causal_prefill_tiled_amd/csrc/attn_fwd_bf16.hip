@@ -87,7 +87,7 @@ __global__ void __launch_bounds__(512) bf16_causal_fwd(Bf16Params a) {
     constexpr int KPT = T::K_CHUNKS / NT;         // K chunks staged per G0 thread
     constexpr int VPT = T::V_CHUNKS / NT;         // V chunks staged per G1 thread
     constexpr int SPT = KPT > VPT ? KPT : VPT;
-    static_assert(T::K_CHUNKS == 4 * KB * KPT && T::V_CHUNKS == 4 * KB * VPT, "4 threads per staged row");
+    static_assert(T::K_CHUNKS % NT == 0 && T::V_CHUNKS % NT == 0, "staging split");
 
     __shared__ __attribute__((aligned(16))) uint8_t smem_raw[T::LDS_BYTES];
     ATTN_LDS uint8_t* smem = (ATTN_LDS uint8_t*)smem_raw;
@@ -134,44 +134,57 @@ __global__ void __launch_bounds__(512) bf16_causal_fwd(Bf16Params a) {
     }
 
     // ---- staging.  G0 moves K blocks, G1 V blocks: HBM -> registers (gload, one
-    // iteration ahead) -> LDS (lstore).  Thread tg of a group takes row tg/4 of the
-    // tile and its 16-byte chunks at LDS positions 4i + tg%4, so chunk i lies at a
-    // constant offset from one LDS base and one of two global bases: K rows are
-    // padded, not swizzled (global chunk = position); a V row stores global chunk
-    // pos ^ v_swz16(row) at position pos, which maps even and odd i to two bases
-    // 128(i/2) apart.
+    // iteration ahead) -> LDS (lstore).  TPR consecutive threads cover TPR
+    // consecutive 16-byte chunks of a row (16 for V and d_qk = 128 K rows, 8 for
+    // d_qk = 192), so each 16-lane LDS store pass writes one or two rows: distinct
+    // bank groups (K rows are padded by 16 bytes, V chunks XOR-swizzled within the
+    // row).  Load i covers row pass i / CG (NT / TPR rows apart) and chunk group
+    // i % CG (TPR chunks apart); the row pass is added to the vector offset, which
+    // alone is range-checked.
+    constexpr int K_TPR = (DQK / 8) % 16 == 0 ? 16 : 8;   // K threads per row
+    constexpr int K_CG = DQK / 8 / K_TPR;                  // chunk groups per K row
+    static_assert(K_CG * (KB / (NT / K_TPR)) == KPT && (NT / 16) * 4 == KB && VPT == 4, "staging split");
     i32x4 st[SPT];
-    int g_even, g_odd, s_base;
+    int g_base, s_base, g_step;
     {
-        const int row = tg >> 2, t = tg & 3;
+        const int tpr = grp == 0 ? K_TPR : 16;
+        const int row = tg / tpr, cc = tg % tpr;
         if (grp == 0) {
-            g_even = row * k_row + 16 * t;
-            g_odd = g_even + 64;
-            s_base = row * T::K_STRIDE + 16 * t;
+            g_base = row * k_row + 16 * cc;
+            s_base = row * T::K_STRIDE + 16 * cc;
+            g_step = (NT / K_TPR) * k_row;
         } else {
-            const int s2 = (row >> 1) & 1;
-            const int g0 = row * v_row + 16 * (t ^ ((row & 1) << 1));
-            g_even = g0 + 64 * s2;
-            g_odd = g0 + 64 * (1 - s2);
-            s_base = T::OFF_V + row * 256 + 16 * t;
+            g_base = row * v_row + 16 * cc;
+            s_base = T::OFF_V + row * 256 + 16 * (cc ^ v_swz16(row));   // row%4 is the same in every pass
+            g_step = 16 * v_row;
         }
     }
     // Every block index is loaded (blocks past the last one read zeros through an
     // empty range), so the staging steps need no guards.
     auto gload = [&](int j) {
         const int rows = max(min(S - j * KB, KB), 0);
-        const bool k = grp == 0;
-        const auto r = k ? buffer_rsrc(kbase + (int64_t)j * KB * k_row, rows * k_row)
-                         : buffer_rsrc(vbase + (int64_t)j * KB * v_row, rows * v_row);
+        if (grp == 0) {
+            const auto r = buffer_rsrc(kbase + (int64_t)j * KB * k_row, rows * k_row);
 #pragma unroll
-        for (int i = 0; i < SPT; ++i)
-            if (i < (k ? KPT : VPT)) st[i] = buffer_load16(r, ((i & 1) ? g_odd : g_even) + 128 * (i >> 1));
+            for (int i = 0; i < KPT; ++i)
+                st[i] = buffer_load16(r, g_base + (i / K_CG) * g_step + 16 * K_TPR * (i % K_CG));
+        } else {
+            const auto r = buffer_rsrc(vbase + (int64_t)j * KB * v_row, rows * v_row);
+#pragma unroll
+            for (int i = 0; i < VPT; ++i) st[i] = buffer_load16(r, g_base + i * g_step);
+        }
     };
     auto lstore = [&](int j) {   // G0: K slot j%2, G1: V slot j%2
-        ATTN_LDS uint8_t* base = smem + s_base + (j & 1) * (grp == 0 ? T::K_BYTES : T::V_BYTES);
+        if (grp == 0) {
+            ATTN_LDS uint8_t* base = smem + s_base + (j & 1) * T::K_BYTES;
 #pragma unroll
-        for (int i = 0; i < SPT; ++i)
-            if (i < (grp == 0 ? KPT : VPT)) lds_store16(base + 64 * i, st[i]);
+            for (int i = 0; i < KPT; ++i)
+                lds_store16(base + (i / K_CG) * (NT / K_TPR) * T::K_STRIDE + 16 * K_TPR * (i % K_CG), st[i]);
+        } else {
+            ATTN_LDS uint8_t* base = smem + s_base + (j & 1) * T::V_BYTES;
+#pragma unroll
+            for (int i = 0; i < VPT; ++i) lds_store16(base + i * 16 * 256, st[i]);
+        }
     };
 
     // ---- V^T construction.  The P.V A operand for d tile dt and K-step ks (keys
