@@ -129,6 +129,23 @@ def test_bf16_full_tensor(shape):
     assert np.all(np.abs(got[:, 0] - v0) <= 2.0 ** -7 * np.abs(v0) + 1e-30)
 
 
+@pytest.mark.parametrize("dqk", [128, 192])
+def test_bf16_deterministic_over_repeated_launches(dqk):
+    w = custom(1, 8, 2, 2048, dqk)
+    d = W.make_bf16(w, seed=77)
+    q, k, v = (d[n].to("cuda:0") for n in ("q", "k", "v"))
+    out = torch.empty((1, 2048, 8, 128), dtype=torch.bfloat16, device="cuda:0")
+    first, mismatches = None, 0
+    for _ in range(200):
+        binding.attn_fwd_bf16(q, k, v, out=out)
+        if first is None:
+            first = out.view(torch.int16).clone()
+        elif not torch.equal(out.view(torch.int16), first):
+            mismatches += 1
+    torch.cuda.synchronize()
+    assert mismatches == 0
+
+
 @pytest.mark.parametrize("name", ["qwen", "mla"])
 def test_bf16_full_size_sampled(name):
     w = W.WORKLOADS[name]
