@@ -21,6 +21,8 @@ Modules:
 * ``e4m3``        - OCP e4m3fn decode / round-to-nearest-even encode, bf16 RNE.
 * ``attention64`` - the plain definition of causal softmax attention in fp64 on
   dequantised inputs (the target the method approximates).
+* ``rotate``      - the Hadamard rotation of Q and K before their per-tensor FP8
+  quantisation, and that quantisation.
 * ``emulate``     - the FP8 method step by step (per-64-key-block power-of-2
   scaling, exact-exp or Lean-P probabilities rounded to e4m3, normalisation by
   the sum of the rounded probabilities), in fp64 except where the method rounds.
