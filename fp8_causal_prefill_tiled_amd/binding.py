@@ -19,7 +19,7 @@ ATTN_OK, ATTN_E_INVALID_ARG, ATTN_E_UNSUPPORTED, ATTN_E_HIP = 0, 1, 2, 3
 P_EXACT, P_LEAN = 0, 1
 _P_MODES = {"exact": P_EXACT, "lean": P_LEAN, P_EXACT: P_EXACT, P_LEAN: P_LEAN}
 
-_EXPORTS = ("attn_fwd_fp8", "attn_fwd_bf16", "attn_last_error", "attn_abi_version")
+_EXPORTS = ("attn_fwd_fp8", "attn_fwd_bf16", "attn_rotate_quant_bf16", "attn_last_error", "attn_abi_version")
 
 
 class AttnError(RuntimeError):
@@ -48,6 +48,8 @@ def load_library():
     lib.attn_fwd_fp8.restype = i
     lib.attn_fwd_bf16.argtypes = [vp, vp, vp, vp, f, i, i, i, i, i, i, i, vp]
     lib.attn_fwd_bf16.restype = i
+    lib.attn_rotate_quant_bf16.argtypes = [vp, vp, vp, i, i, i, i, vp]
+    lib.attn_rotate_quant_bf16.restype = i
     lib.attn_last_error.argtypes = []
     lib.attn_last_error.restype = ctypes.c_char_p
     lib.attn_abi_version.argtypes = []
@@ -96,6 +98,27 @@ def attn_fwd_fp8_raw(q, k, v, o, q_scale, k_scale, v_scale, softmax_scale, B, Hq
 
 def attn_fwd_bf16_raw(q, k, v, o, softmax_scale, B, Hq, Hkv, S, d_qk, d_v, causal, stream=0):
     return load_library().attn_fwd_bf16(q, k, v, o, softmax_scale, B, Hq, Hkv, S, d_qk, d_v, causal, stream)
+
+
+def attn_rotate_quant_bf16_raw(x, x8, scale, B, S, H, d, stream=0):
+    return load_library().attn_rotate_quant_bf16(x, x8, scale, B, S, H, d, stream)
+
+
+def rotate_quant_bf16(x, out=None, scale=None, stream=None):
+    """Hadamard-rotate a bf16 (B,S,H,d) Q or K tensor along d and quantise it per tensor
+    to e4m3.  Returns (codes: uint8 (B,S,H,d), scale: one-element float32 device tensor)."""
+    B, S, H, d = _bshd(x, "x")
+    if x.dtype != torch.bfloat16:
+        raise TypeError(f"x must be bfloat16, got {x.dtype}")
+    if out is None:
+        out = torch.empty(x.shape, dtype=torch.uint8, device=x.device)
+    elif out.shape != x.shape or out.dtype != torch.uint8 or not out.is_contiguous():
+        raise ValueError("out must be a contiguous uint8 tensor of x's shape")
+    if scale is None:
+        scale = torch.empty(1, dtype=torch.float32, device=x.device)
+    _check(load_library().attn_rotate_quant_bf16(x.data_ptr(), out.data_ptr(), scale.data_ptr(), B, S, H, d,
+                                                 _stream_ptr(stream, x.device)))
+    return out, scale
 
 
 def attn_fwd_fp8(q8, k8, v8, q_scale, k_scale, v_scale, softmax_scale=None, causal=True,

@@ -17,7 +17,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libattnfwd.so")
-SOURCES = ["api.cpp", "attn_fwd_fp8.hip", "attn_fwd_bf16.hip"]
+SOURCES = ["api.cpp", "attn_fwd_fp8.hip", "attn_fwd_bf16.hip", "rotate_quant.hip"]
 ARCH = "gfx950"
 
 

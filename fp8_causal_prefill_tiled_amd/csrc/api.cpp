@@ -100,6 +100,24 @@ int attn_fwd_bf16(const void* q, const void* k, const void* v, void* o, float so
     return finish(attnfwd::launch_bf16(p), who);
 }
 
+int attn_rotate_quant_bf16(const void* x, void* x8, float* scale, int B, int S, int H, int d,
+                           hipStream_t stream) {
+    const char* who = "attn_rotate_quant_bf16";
+    if (B < 0 || S < 0 || H <= 0) return fail(ATTN_E_INVALID_ARG, "%s: B=%d S=%d H=%d out of range", who, B, S, H);
+    if (d != 128 && d != 192) return fail(ATTN_E_UNSUPPORTED, "%s: d=%d unsupported (128 or 192)", who, d);
+    if (!scale) return fail(ATTN_E_INVALID_ARG, "%s: null scale pointer", who);
+    const int64_t n_el = (int64_t)B * S * H * d;
+    if (n_el * 2 > ((int64_t)1 << 31)) return fail(ATTN_E_UNSUPPORTED, "%s: tensor of %lld elements too large", who, (long long)n_el);
+    if (n_el > 0) {
+        if (!x || !x8) return fail(ATTN_E_INVALID_ARG, "%s: null tensor pointer", who);
+        if (!aligned16(x) || !aligned16(x8)) return fail(ATTN_E_INVALID_ARG, "%s: tensor pointers must be 16-byte aligned", who);
+        if (overlaps(x8, (size_t)n_el, x, (size_t)n_el * 2) || overlaps(scale, 4, x, (size_t)n_el * 2) ||
+            overlaps(scale, 4, x8, (size_t)n_el))
+            return fail(ATTN_E_INVALID_ARG, "%s: output overlaps an input", who);
+    }
+    return finish(attnfwd::launch_rotate_quant(x, x8, scale, n_el, d, stream), who);
+}
+
 const char* attn_last_error(void) { return g_err; }
 
 int attn_abi_version(void) { return 100; }

@@ -20,5 +20,8 @@ struct Problem {
 
 hipError_t launch_fp8(const Problem& p);
 hipError_t launch_bf16(const Problem& p);
+// Hadamard rotation + per-tensor e4m3 quantisation of n_el bf16 values (rows of
+// d elements); scale points to one device float.
+hipError_t launch_rotate_quant(const void* x, void* x8, float* scale, int64_t n_el, int d, hipStream_t s);
 
 }  // namespace attnfwd

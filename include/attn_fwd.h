@@ -101,6 +101,30 @@ int attn_fwd_bf16(const void* q, const void* k, const void* v, void* o,
                   int B, int Hq, int Hkv, int S, int d_qk, int d_v,
                   int causal, hipStream_t stream);
 
+/*
+ * Hadamard rotation and per-tensor FP8 quantisation of a Q or K tensor ("Zyphra
+ * ZYFA: FP8 FlashAttention for AMD MI355X, Up to 1.76x Faster", section "How
+ * accurate is ZYFA's FP8 attention?": rotating Q and K by a Hadamard matrix
+ * before quantisation cuts the input error to about half).
+ *
+ * x:     bfloat16 (B, S, H, d), contiguous, 16-byte aligned; d = 128 or 192.
+ * x8:    output e4m3fn bytes (B, S, H, d), 16-byte aligned, not overlapping x.
+ * scale: output, device pointer to one float: amax / 448 of the rotated tensor
+ *        (1 if it is all zero); dequantised rotated value = scale * decode(byte).
+ *
+ * Each (token, head) vector is multiplied along d by the orthonormal
+ * Sylvester-Hadamard matrix H_n / sqrt(n): n = 128 for d = 128, three blocks of
+ * n = 64 for d = 192.  The codes are e4m3 RNE(rotated / scale), saturating at
+ * +-448.  H is orthogonal, so rotating both Q and K leaves the attention scores
+ * unchanged: pass the rotated codes and their scales to attn_fwd_fp8 (V is not
+ * rotated).  Enqueues four small kernels on stream; allocates nothing; the
+ * caller owns x, x8 and scale.  Errors as for attn_fwd_fp8: ATTN_E_INVALID_ARG
+ * for null or misaligned pointers, negative sizes or overlapping buffers,
+ * ATTN_E_UNSUPPORTED for d other than 128 or 192 or a tensor above 2^31 bytes.
+ */
+int attn_rotate_quant_bf16(const void* x, void* x8, float* scale, int B, int S, int H, int d,
+                           hipStream_t stream);
+
 /* Message for the calling thread's last non-OK status ("" if none).  The
  * returned storage is thread-local and valid until that thread's next call. */
 const char* attn_last_error(void);

@@ -95,3 +95,23 @@ def test_python_binding_rejects_bad_tensors(lib):
         binding.attn_fwd_fp8(x.float(), x, x, 1.0, 1.0, 1.0)
     with pytest.raises(TypeError):
         binding.attn_fwd_bf16(x, x, x)
+
+
+def rotq(**kw):
+    a = dict(x=Q, x8=K, scale=V, B=1, S=64, H=2, d=128)
+    a.update(kw)
+    return binding.attn_rotate_quant_bf16_raw(**a)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(x=0), INVALID), (dict(x8=0), INVALID), (dict(scale=0), INVALID),
+    (dict(B=-1), INVALID), (dict(S=-3), INVALID), (dict(H=0), INVALID),
+    (dict(d=96), UNSUPPORTED), (dict(d=64), UNSUPPORTED), (dict(d=256), UNSUPPORTED),
+    (dict(x=Q + 8), INVALID), (dict(x8=K + 4), INVALID),
+    (dict(x8=Q + 4096), INVALID),               # codes overlap the input
+    (dict(scale=Q + 64), INVALID),              # scale inside the input
+    (dict(B=1 << 20, S=1 << 10, H=8), UNSUPPORTED),
+])
+def test_rotate_quant_rejects(lib, kw, status):
+    assert rotq(**kw) == status
+    assert binding.attn_last_error()
