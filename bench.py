@@ -37,6 +37,8 @@ def parse():
     ap.add_argument("--no-both-modes", dest="both_modes", action="store_false")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--no-rotate", action="store_true",
+                    help="skip timing the Hadamard rotation + quantisation of Q and K")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
                     help="after timing, run one device-to-device copy of this many MiB "
                          "(a known-size kernel for scaling HBM byte counters)")
@@ -92,6 +94,39 @@ def time_launches(fn, steps, warmup, stream):
     wall = time.perf_counter() - t0
     per = sorted(s.elapsed_time(e) for s, e in zip(starts, ends))   # ms, HIP events on the launch stream
     return wall, per
+
+
+HBM_PEAK_GBPS = 8000.0
+
+
+def rotate_quant_timing(w, steps, warmup, stream, attn_ms):
+    """Time attn_rotate_quant_bf16 on bf16 tensors of the workload's Q and K shapes
+    (seeded N(0,1), resident in HBM).  HBM roofline of the pass: algorithmic bytes =
+    the bf16 tensor read once + one e4m3 byte per element written."""
+    import torch
+    from fp8_causal_prefill_tiled_amd import binding
+    dev = torch.device("cuda:0")
+    g = torch.Generator(device=dev)
+    g.manual_seed(20261202)
+    res = {}
+    for name, h in (("q", w.Hq), ("k", w.Hkv)):
+        x = torch.randn((w.B, w.S, h, w.d_qk), generator=g, device=dev, dtype=torch.float32).to(torch.bfloat16)
+        out = torch.empty(x.shape, dtype=torch.uint8, device=dev)
+        sc = torch.empty(1, dtype=torch.float32, device=dev)
+        _, per = time_launches(lambda: binding.rotate_quant_bf16(x, out=out, scale=sc, stream=stream),
+                               steps, warmup, stream)
+        ms = sum(per) / len(per)
+        nbytes = x.numel() * 3
+        res[name] = {"shape": list(x.shape), "kernel_ms_avg": ms, "algorithmic_bytes": nbytes,
+                     "achieved_GBps": nbytes / (ms * 1e-3) / 1e9}
+        del x, out
+    total_ms = res["q"]["kernel_ms_avg"] + res["k"]["kernel_ms_avg"]
+    total_bytes = res["q"]["algorithmic_bytes"] + res["k"]["algorithmic_bytes"]
+    achieved = total_bytes / (total_ms * 1e-3) / 1e9
+    return {"kernels": "rq_amax + rq_quant (+ two 1-thread kernels), Q then K", "q": res["q"], "k": res["k"],
+            "ms_q_plus_k": total_ms, "fraction_of_attention_time": total_ms / attn_ms,
+            "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                         "frac": achieved / HBM_PEAK_GBPS, "traffic": None}}
 
 
 def cpu_baseline(w, d, out_gpu, seconds, dtype):
@@ -223,6 +258,10 @@ def main():
         out_np = out.float().cpu().numpy()
         cpu = cpu_baseline(w, d, out_np, args.cpu_seconds, args.dtype)
 
+    rot = None
+    if args.dtype == "fp8" and not args.no_rotate:
+        rot = rotate_quant_timing(w, args.steps, args.warmup, stream, head["kernel_ms_avg"])
+
     pages = PAGES_TFLOPS.get((w.name, args.dtype))
     res = {
         "metric": METRIC,
@@ -247,6 +286,7 @@ def main():
                      "traffic": measured_traffic(w.name, modes[0]) if args.dtype == "fp8" else None,
                      "kernel": f"{args.dtype}_causal_fwd", "per_launch_tflop": flops / 1e12},
         "paths": paths,
+        "rotate_quant": rot,
         "sclk_mhz": {"before": clk_before, "after": clk_after},
         "cpu_baseline": cpu,
     }

@@ -13,13 +13,13 @@
 // Layout: rows are contiguous and d is a multiple of n, so the tensor is a
 // sequence of n-element blocks.  LB = n/8 consecutive lanes hold one block, 8
 // bf16 per lane (one 16-byte load); the fast Walsh-Hadamard transform runs its 3
-// low butterfly stages inside the lane and log2(LB) stages across lanes (xor
-// shuffles within the block's aligned lane group).  Four stream-ordered launches:
-// zero the amax cell; rotate and reduce max|y| (one atomic max per wave on the
-// float's bits, order-preserving for non-negative floats); rotate again and
-// quantise with the final scale; turn the cell into the scale.  The work is HBM
-// streaming: each of the two passes reads the bf16 tensor once, the second
-// writes one byte per element.
+// low butterfly stages inside the lane and log2(LB) stages across lanes (lane-xor
+// moves within the block's aligned lane group, by DPP).  Four stream-ordered launches:
+// zero the amax cell; rotate and reduce max|y| (per wave, then an atomic max on
+// the float's bits, order-preserving for non-negative floats, skipped when the
+// cell already holds more); rotate again and quantise with the final scale; turn
+// the cell into the scale.  The work is HBM streaming: each of the two passes
+// reads the bf16 tensor once, the second writes one byte per element.
 #include "common.h"
 #include "launch.h"
 
@@ -29,29 +29,66 @@ namespace {
 constexpr float kE4M3Max = 448.0f;
 constexpr int kThreads = 256;
 
-// Unnormalised transform of one block, y_i = sum_j (-1)^popcount(i & j) x_j: bit
-// b of the element index is one butterfly stage (lower index a + b, upper a - b).
-// Lane t of the block holds elements 8t .. 8t+7.
-template <int LB>
-__device__ __forceinline__ void fwht(float (&x)[8], int t) {
+// Value of lane i ^ M (M = 1, 2, 4, 8) by data-parallel-primitive moves, no LDS:
+// quad permutations give xor 1, 2 and 3; the half-row mirror is xor 7 and the row
+// mirror xor 15 within 16 lanes, so xor 4 = (xor 7 then xor 3) and xor 8 = (xor 15
+// then xor 7).
+template <int M>
+__device__ __forceinline__ float xor_lane(float v) {
+    constexpr int kQuadXor1 = 0xB1, kQuadXor2 = 0x4E, kQuadXor3 = 0x1B, kRowMirror = 0x140, kRowHalfMirror = 0x141;
+    int x = __float_as_int(v);
+    if constexpr (M == 1) {
+        x = __builtin_amdgcn_update_dpp(0, x, kQuadXor1, 0xF, 0xF, false);
+    } else if constexpr (M == 2) {
+        x = __builtin_amdgcn_update_dpp(0, x, kQuadXor2, 0xF, 0xF, false);
+    } else if constexpr (M == 4) {
+        x = __builtin_amdgcn_update_dpp(0, x, kRowHalfMirror, 0xF, 0xF, false);
+        x = __builtin_amdgcn_update_dpp(0, x, kQuadXor3, 0xF, 0xF, false);
+    } else {
+        static_assert(M == 8, "xor within 16 lanes");
+        x = __builtin_amdgcn_update_dpp(0, x, kRowMirror, 0xF, 0xF, false);
+        x = __builtin_amdgcn_update_dpp(0, x, kRowHalfMirror, 0xF, 0xF, false);
+    }
+    return __int_as_float(x);
+}
+
+// One cross-lane butterfly stage over the U blocks a lane holds: partner lane
+// t ^ M (lower index a + b, upper a - b).
+template <int M, int NU>
+__device__ __forceinline__ void cross_stage(float (&x)[NU][8], int t) {
+    const bool upper = (t & M) != 0;
+#pragma unroll
+    for (int u = 0; u < NU; ++u)
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const float p = xor_lane<M>(x[u][i]);
+            x[u][i] = upper ? p - x[u][i] : x[u][i] + p;
+        }
+}
+
+// Unnormalised transform of NU blocks at once (each stage runs over all of them
+// before the next, so consecutive dependent lane moves are far apart), y_i =
+// sum_j (-1)^popcount(i & j) x_j: bit b of the element index is one butterfly
+// stage (lower index a + b, upper a - b).  Lane t of a block holds elements
+// 8t .. 8t+7.
+template <int LB, int NU>
+__device__ __forceinline__ void fwht(float (&x)[NU][8], int t) {
 #pragma unroll
     for (int h = 1; h < 8; h <<= 1)
 #pragma unroll
-        for (int i = 0; i < 8; ++i)
-            if (!(i & h)) {
-                const float a = x[i], b = x[i + h];
-                x[i] = a + b;
-                x[i + h] = a - b;
-            }
+        for (int u = 0; u < NU; ++u)
 #pragma unroll
-    for (int m = 1; m < LB; m <<= 1) {
-        const bool upper = (t & m) != 0;
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const float p = __shfl_xor(x[i], m, 64);
-            x[i] = upper ? p - x[i] : x[i] + p;
-        }
-    }
+            for (int i = 0; i < 8; ++i)
+                if (!(i & h)) {
+                    const float a = x[u][i], b = x[u][i + h];
+                    x[u][i] = a + b;
+                    x[u][i + h] = a - b;
+                }
+    static_assert(LB == 8 || LB == 16, "blocks of 64 or 128 elements");
+    cross_stage<1>(x, t);
+    cross_stage<2>(x, t);
+    cross_stage<4>(x, t);
+    if constexpr (LB == 16) cross_stage<8>(x, t);
 }
 
 // The 8 bf16 of lane t of block blk as fp32 (zeros past the end; every lane then
@@ -74,26 +111,33 @@ constexpr float inv_sqrt_nb() {
 
 __global__ void rq_init(unsigned* cell) { *cell = 0u; }
 
+// Each wave takes U consecutive 1 KiB steps (BPW blocks each, contiguous in
+// memory) and issues all U loads before using any, so every lane keeps U 16-byte
+// loads in flight.
+constexpr int U = 4;
+
 template <int NB>
 __global__ void __launch_bounds__(kThreads) rq_amax(const __bf16* __restrict__ x, int64_t nblocks, unsigned* cell) {
     constexpr int LB = NB / 8, BPW = 64 / LB;
     const int lane = threadIdx.x & 63, t = lane % LB;
     const int64_t wave = ((int64_t)blockIdx.x * kThreads + threadIdx.x) >> 6;
-    const int64_t nwave = ((int64_t)gridDim.x * kThreads) >> 6;
-    float m = 0.0f;
-    for (int64_t b0 = wave * BPW; b0 < nblocks; b0 += nwave * BPW) {
-        float v[8];
-        load_block(x, b0 + lane / LB, nblocks, NB, t, v);
-        fwht<LB>(v, t);
+    float v[U][8];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) m = fmaxf(m, fabsf(v[i]));
-    }
+    for (int u = 0; u < U; ++u) load_block(x, (wave * U + u) * BPW + lane / LB, nblocks, NB, t, v[u]);
+    fwht<LB>(v, t);
+    float m = 0.0f;
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+#pragma unroll
+        for (int i = 0; i < 8; ++i) m = fmaxf(m, fabsf(v[u][i]));
     // max |y| of the normalised rotation: scaling by a positive constant commutes
     // with the maximum, rounding included
     m *= inv_sqrt_nb<NB>();
 #pragma unroll
     for (int o = 32; o >= 1; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
-    if (lane == 0) atomicMax(cell, __float_as_uint(m));
+    // the running maximum is usually larger already: read it and skip the atomic
+    if (lane == 0 && __float_as_uint(m) > __hip_atomic_load(cell, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT))
+        atomicMax(cell, __float_as_uint(m));
 }
 
 __device__ __forceinline__ float scale_of(float amax) { return amax > 0.0f ? amax / kE4M3Max : 1.0f; }
@@ -104,16 +148,19 @@ __global__ void __launch_bounds__(kThreads) rq_quant(const __bf16* __restrict__ 
     constexpr int LB = NB / 8, BPW = 64 / LB;
     const int lane = threadIdx.x & 63, t = lane % LB;
     const int64_t wave = ((int64_t)blockIdx.x * kThreads + threadIdx.x) >> 6;
-    const int64_t nwave = ((int64_t)gridDim.x * kThreads) >> 6;
-    const float scale = scale_of(__uint_as_float(*cell));
-    for (int64_t b0 = wave * BPW; b0 < nblocks; b0 += nwave * BPW) {
-        const int64_t blk = b0 + lane / LB;
-        float v[8];
-        load_block(x, blk, nblocks, NB, t, v);
-        fwht<LB>(v, t);
+    float v[U][8];
+#pragma unroll
+    for (int u = 0; u < U; ++u) load_block(x, (wave * U + u) * BPW + lane / LB, nblocks, NB, t, v[u]);
+    // one multiply per element by 1/(sqrt(n) scale): within an ulp of dividing the
+    // normalised value by the scale, so the rounding to e4m3 can differ only at ties
+    const float f = inv_sqrt_nb<NB>() / scale_of(__uint_as_float(*cell));
+    fwht<LB>(v, t);
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        const int64_t blk = (wave * U + u) * BPW + lane / LB;
         float q[8];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) q[i] = fminf(fmaxf(v[i] * inv_sqrt_nb<NB>() / scale, -kE4M3Max), kE4M3Max);
+        for (int i = 0; i < 8; ++i) q[i] = fminf(fmaxf(v[u][i] * f, -kE4M3Max), kE4M3Max);
         int w0 = __builtin_amdgcn_cvt_pk_fp8_f32(q[0], q[1], 0, false);
         w0 = __builtin_amdgcn_cvt_pk_fp8_f32(q[2], q[3], w0, true);
         int w1 = __builtin_amdgcn_cvt_pk_fp8_f32(q[4], q[5], 0, false);
@@ -130,12 +177,13 @@ template <int NB>
 hipError_t launch_t(const __bf16* x, uint8_t* x8, unsigned* cell, int64_t n_el, hipStream_t s) {
     const int64_t nblocks = n_el / NB;
     constexpr int BPW = 64 / (NB / 8);
+    constexpr int64_t per_wg = (int64_t)BPW * U * (kThreads / 64);   // blocks per workgroup
     hipLaunchKernelGGL(rq_init, dim3(1), dim3(1), 0, s, cell);
     if (nblocks > 0) {
-        const int64_t want = (nblocks + BPW * (kThreads / 64) - 1) / (BPW * (kThreads / 64));
-        const unsigned grid = (unsigned)(want < 4096 ? want : 4096);   // grid-stride beyond 4096 workgroups
-        hipLaunchKernelGGL((rq_amax<NB>), dim3(grid), dim3(kThreads), 0, s, x, nblocks, cell);
-        hipLaunchKernelGGL((rq_quant<NB>), dim3(grid), dim3(kThreads), 0, s, x, nblocks, cell, x8);
+        const int64_t grid = (nblocks + per_wg - 1) / per_wg;
+        if (grid > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+        hipLaunchKernelGGL((rq_amax<NB>), dim3((unsigned)grid), dim3(kThreads), 0, s, x, nblocks, cell);
+        hipLaunchKernelGGL((rq_quant<NB>), dim3((unsigned)grid), dim3(kThreads), 0, s, x, nblocks, cell, x8);
     }
     hipLaunchKernelGGL(rq_finish, dim3(1), dim3(1), 0, s, cell);
     return hipGetLastError();
