@@ -15,9 +15,9 @@
 // bf16 per lane (one 16-byte load); the fast Walsh-Hadamard transform runs its 3
 // low butterfly stages inside the lane and log2(LB) stages across lanes (lane-xor
 // moves within the block's aligned lane group, by DPP).  Four stream-ordered launches:
-// zero the amax cell; rotate and reduce max|y| (per wave, then an atomic max on
-// the float's bits, order-preserving for non-negative floats, skipped when the
-// cell already holds more); rotate again and quantise with the final scale; turn
+// zero the amax cell; rotate and reduce max|y| (per workgroup, then an atomic max
+// on the float's bits, order-preserving for non-negative floats, skipped when
+// the cell already holds more); rotate again and quantise with the final scale; turn
 // the cell into the scale.  The work is HBM streaming: each of the two passes
 // reads the bf16 tensor once, the second writes one byte per element.
 #include "common.h"
@@ -116,28 +116,44 @@ __global__ void rq_init(unsigned* cell) { *cell = 0u; }
 // loads in flight.
 constexpr int U = 4;
 
+// The max pass runs a fixed grid of grid-stride workgroups: each wave loops over
+// groups of U steps, and each workgroup ends with one reduction and at most one
+// atomic (these are device-scope operations on one address, served beyond the
+// per-XCD L2s, so their number is kept small).
+constexpr int kAmaxGrid = 2048;
+
 template <int NB>
 __global__ void __launch_bounds__(kThreads) rq_amax(const __bf16* __restrict__ x, int64_t nblocks, unsigned* cell) {
     constexpr int LB = NB / 8, BPW = 64 / LB;
     const int lane = threadIdx.x & 63, t = lane % LB;
     const int64_t wave = ((int64_t)blockIdx.x * kThreads + threadIdx.x) >> 6;
-    float v[U][8];
-#pragma unroll
-    for (int u = 0; u < U; ++u) load_block(x, (wave * U + u) * BPW + lane / LB, nblocks, NB, t, v[u]);
-    fwht<LB>(v, t);
+    const int64_t nwave = ((int64_t)gridDim.x * kThreads) >> 6;
     float m = 0.0f;
+    for (int64_t w0 = wave * U; w0 * BPW < nblocks; w0 += nwave * U) {
+        float v[U][8];
 #pragma unroll
-    for (int u = 0; u < U; ++u)
+        for (int u = 0; u < U; ++u) load_block(x, (w0 + u) * BPW + lane / LB, nblocks, NB, t, v[u]);
+        fwht<LB>(v, t);
 #pragma unroll
-        for (int i = 0; i < 8; ++i) m = fmaxf(m, fabsf(v[u][i]));
+        for (int u = 0; u < U; ++u)
+#pragma unroll
+            for (int i = 0; i < 8; ++i) m = fmaxf(m, fabsf(v[u][i]));
+    }
     // max |y| of the normalised rotation: scaling by a positive constant commutes
     // with the maximum, rounding included
     m *= inv_sqrt_nb<NB>();
 #pragma unroll
     for (int o = 32; o >= 1; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
-    // the running maximum is usually larger already: read it and skip the atomic
-    if (lane == 0 && __float_as_uint(m) > __hip_atomic_load(cell, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT))
-        atomicMax(cell, __float_as_uint(m));
+    __shared__ float wmax[kThreads / 64];
+    if (lane == 0) wmax[threadIdx.x >> 6] = m;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+#pragma unroll
+        for (int i = 1; i < kThreads / 64; ++i) m = fmaxf(m, wmax[i]);
+        // the running maximum is usually larger already: read it and skip the atomic
+        if (__float_as_uint(m) > __hip_atomic_load(cell, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT))
+            atomicMax(cell, __float_as_uint(m));
+    }
 }
 
 __device__ __forceinline__ float scale_of(float amax) { return amax > 0.0f ? amax / kE4M3Max : 1.0f; }
@@ -182,7 +198,8 @@ hipError_t launch_t(const __bf16* x, uint8_t* x8, unsigned* cell, int64_t n_el, 
     if (nblocks > 0) {
         const int64_t grid = (nblocks + per_wg - 1) / per_wg;
         if (grid > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-        hipLaunchKernelGGL((rq_amax<NB>), dim3((unsigned)grid), dim3(kThreads), 0, s, x, nblocks, cell);
+        const unsigned agrid = (unsigned)(grid < kAmaxGrid ? grid : kAmaxGrid);
+        hipLaunchKernelGGL((rq_amax<NB>), dim3(agrid), dim3(kThreads), 0, s, x, nblocks, cell);
         hipLaunchKernelGGL((rq_quant<NB>), dim3((unsigned)grid), dim3(kThreads), 0, s, x, nblocks, cell, x8);
     }
     hipLaunchKernelGGL(rq_finish, dim3(1), dim3(1), 0, s, cell);
