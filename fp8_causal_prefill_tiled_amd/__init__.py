@@ -8,7 +8,7 @@ call into the attention entry points fails loudly if the library is missing.
 """
 from . import workloads  # noqa: F401
 
-_BINDING_NAMES = {"attn_fwd_fp8", "attn_fwd_bf16", "attn_last_error", "library_path",
+_BINDING_NAMES = {"attn_fwd_fp8", "attn_fwd_bf16", "rotate_quant_bf16", "attn_last_error", "library_path",
                   "load_library", "P_EXACT", "P_LEAN", "AttnError", "exported_symbols"}
 
 
