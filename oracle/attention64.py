@@ -82,6 +82,32 @@ def attention_fp64(q, k, v, sm_scale=None, causal=True, rows=None, chunk=512):
     return out
 
 
+def lse_fp64(q, k, sm_scale=None, causal=True, rows=None, chunk=512):
+    """Natural-log softmax normaliser of each query row, ln sum_j exp(sm <q_i, k_j>) over
+    the keys the row sees (all keys, or j <= i when causal), in fp64.  Returns
+    (B, Hq, len(rows)): the layout attention libraries return it in."""
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    B, S, Hq, dqk = q.shape
+    Hkv = k.shape[2]
+    sm = 1.0 / np.sqrt(dqk) if sm_scale is None else float(sm_scale)
+    rows = _rows_of(rows, S)
+    out = np.empty((B, Hq, len(rows)), dtype=np.float64)
+    keys = np.arange(S)
+    for b in range(B):
+        for h in range(Hq):
+            kk = k[b, :, kv_head(h, Hq, Hkv), :]
+            for c0 in range(0, len(rows), chunk):
+                r = rows[c0:c0 + chunk]
+                n = (int(r.max()) + 1) if causal else S
+                logits = sm * (q[b, r, h, :] @ kk[:n].T)
+                if causal:
+                    logits = np.where(keys[None, :n] <= r[:, None], logits, -np.inf)
+                m = logits.max(axis=1)
+                out[b, h, c0:c0 + len(r)] = m + np.log(np.exp(logits - m[:, None]).sum(axis=1))
+    return out
+
+
 def attention_weights_fp64(q, k, sm_scale=None, causal=True):
     """The full weight matrix w[b, h, i, j] (small shapes only)."""
     q = np.asarray(q, dtype=np.float64)

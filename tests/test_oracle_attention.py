@@ -11,7 +11,7 @@ import math
 import numpy as np
 import pytest
 
-from oracle.attention64 import attention_fp64, attention_weights_fp64, rel_rms
+from oracle.attention64 import attention_fp64, attention_weights_fp64, lse_fp64, rel_rms
 
 
 def brute_force(q, k, v, sm, causal):
@@ -97,3 +97,39 @@ def test_last_causal_row_equals_noncausal_last_row_and_row_subsets():
 def test_rel_rms():
     a = np.array([3.0, 4.0])
     assert rel_rms(a * 1.01, a) == pytest.approx(0.01)
+
+
+def brute_force_lse(q, k, sm, causal):
+    """Pure-Python log-sum-exp of each row's logits, (B, Hq, S)."""
+    B, S, Hq, dqk = q.shape
+    Hkv = k.shape[2]
+    out = np.zeros((B, Hq, S))
+    for b in range(B):
+        for h in range(Hq):
+            g = h // (Hq // Hkv)
+            for i in range(S):
+                logits = [sm * sum(float(q[b, i, h, c]) * float(k[b, j, g, c]) for c in range(dqk))
+                          for j in (range(i + 1) if causal else range(S))]
+                out[b, h, i] = math.log(sum(math.exp(x) for x in logits))
+    return out
+
+
+@pytest.mark.parametrize("causal", [True, False])
+def test_lse_matches_brute_force(causal):
+    rng = np.random.default_rng(21)
+    q = rng.standard_normal((2, 11, 4, 5)) * 1.5
+    k = rng.standard_normal((2, 11, 2, 5))
+    ours = lse_fp64(q, k, sm_scale=0.6, causal=causal, chunk=3)
+    assert np.max(np.abs(ours - brute_force_lse(q, k, 0.6, causal))) < 1e-12
+
+
+def test_lse_closed_forms():
+    # row 0 of a causal call sees one key: lse = its logit; zero queries: lse = ln(#keys)
+    rng = np.random.default_rng(2)
+    q = rng.standard_normal((1, 6, 2, 4))
+    k = rng.standard_normal((1, 6, 1, 4))
+    lse = lse_fp64(q, k, sm_scale=0.5)
+    assert np.allclose(lse[0, :, 0], 0.5 * (q[0, 0] @ k[0, 0, 0]), atol=1e-14)
+    z = lse_fp64(np.zeros_like(q), k)
+    assert np.allclose(z[0, 0], np.log(np.arange(1, 7)), atol=1e-14)
+    assert np.allclose(lse_fp64(np.zeros_like(q), k, causal=False), np.log(6.0), atol=1e-14)
