@@ -19,7 +19,8 @@ ATTN_OK, ATTN_E_INVALID_ARG, ATTN_E_UNSUPPORTED, ATTN_E_HIP = 0, 1, 2, 3
 P_EXACT, P_LEAN = 0, 1
 _P_MODES = {"exact": P_EXACT, "lean": P_LEAN, P_EXACT: P_EXACT, P_LEAN: P_LEAN}
 
-_EXPORTS = ("attn_fwd_fp8", "attn_fwd_bf16", "attn_rotate_quant_bf16", "attn_last_error", "attn_abi_version")
+_EXPORTS = ("attn_fwd_fp8", "attn_fwd_fp8_lse", "attn_fwd_bf16", "attn_fwd_bf16_lse", "attn_rotate_quant_bf16",
+            "attn_last_error", "attn_abi_version")
 
 
 class AttnError(RuntimeError):
@@ -46,8 +47,12 @@ def load_library():
     vp, f, i = ctypes.c_void_p, ctypes.c_float, ctypes.c_int
     lib.attn_fwd_fp8.argtypes = [vp, vp, vp, vp, f, f, f, f, i, i, i, i, i, i, i, i, vp]
     lib.attn_fwd_fp8.restype = i
+    lib.attn_fwd_fp8_lse.argtypes = [vp, vp, vp, vp, vp, f, f, f, f, i, i, i, i, i, i, i, i, vp]
+    lib.attn_fwd_fp8_lse.restype = i
     lib.attn_fwd_bf16.argtypes = [vp, vp, vp, vp, f, i, i, i, i, i, i, i, vp]
     lib.attn_fwd_bf16.restype = i
+    lib.attn_fwd_bf16_lse.argtypes = [vp, vp, vp, vp, vp, f, i, i, i, i, i, i, i, vp]
+    lib.attn_fwd_bf16_lse.restype = i
     lib.attn_rotate_quant_bf16.argtypes = [vp, vp, vp, i, i, i, i, vp]
     lib.attn_rotate_quant_bf16.restype = i
     lib.attn_last_error.argtypes = []
@@ -96,8 +101,19 @@ def attn_fwd_fp8_raw(q, k, v, o, q_scale, k_scale, v_scale, softmax_scale, B, Hq
                                        B, Hq, Hkv, S, d_qk, d_v, causal, p_mode, stream)
 
 
+def attn_fwd_fp8_lse_raw(q, k, v, o, lse, q_scale, k_scale, v_scale, softmax_scale, B, Hq, Hkv, S, d_qk, d_v,
+                         causal, p_mode, stream=0):
+    return load_library().attn_fwd_fp8_lse(q, k, v, o, lse, q_scale, k_scale, v_scale, softmax_scale,
+                                           B, Hq, Hkv, S, d_qk, d_v, causal, p_mode, stream)
+
+
 def attn_fwd_bf16_raw(q, k, v, o, softmax_scale, B, Hq, Hkv, S, d_qk, d_v, causal, stream=0):
     return load_library().attn_fwd_bf16(q, k, v, o, softmax_scale, B, Hq, Hkv, S, d_qk, d_v, causal, stream)
+
+
+def attn_fwd_bf16_lse_raw(q, k, v, o, lse, softmax_scale, B, Hq, Hkv, S, d_qk, d_v, causal, stream=0):
+    return load_library().attn_fwd_bf16_lse(q, k, v, o, lse, softmax_scale, B, Hq, Hkv, S, d_qk, d_v, causal,
+                                            stream)
 
 
 def attn_rotate_quant_bf16_raw(x, x8, scale, B, S, H, d, stream=0):
@@ -121,12 +137,19 @@ def rotate_quant_bf16(x, out=None, scale=None, stream=None):
     return out, scale
 
 
+def _lse_out(return_lse, B, Hq, S, device):
+    if not return_lse:
+        return None
+    return torch.empty((B, Hq, S), dtype=torch.float32, device=device)
+
+
 def attn_fwd_fp8(q8, k8, v8, q_scale, k_scale, v_scale, softmax_scale=None, causal=True,
-                 p_mode="exact", out=None, stream=None):
-    """Causal FP8 attention; q8/k8/v8 are e4m3fn bytes (uint8 or float8_e4m3fn), (B,S,H,d).
+                 p_mode="exact", out=None, stream=None, return_lse=False):
+    """FP8 attention (causal by default); q8/k8/v8 are e4m3fn bytes (uint8 or float8_e4m3fn), (B,S,H,d).
 
     Returns the bf16 output (B, S, Hq, d_v), enqueued on ``stream`` (default:
-    torch's current stream of the inputs' device).
+    torch's current stream of the inputs' device); with ``return_lse`` returns
+    (out, lse), lse the fp32 (B, Hq, S) natural-log normaliser of every row.
     """
     for t, n in ((q8, "q8"), (k8, "k8"), (v8, "v8")):
         if t.dtype not in (torch.uint8, torch.float8_e4m3fn):
@@ -141,16 +164,19 @@ def attn_fwd_fp8(q8, k8, v8, q_scale, k_scale, v_scale, softmax_scale=None, caus
     elif out.dtype != torch.bfloat16 or tuple(out.shape) != (B, S, Hq, dv) or not out.is_contiguous():
         raise ValueError("out must be a contiguous bf16 tensor of shape (B, S, Hq, d_v)")
     sm = 0.0 if softmax_scale is None else float(softmax_scale)
-    st = attn_fwd_fp8_raw(q8.data_ptr(), k8.data_ptr(), v8.data_ptr(), out.data_ptr(),
-                          float(q_scale), float(k_scale), float(v_scale), sm,
-                          B, Hq, Hkv, S, dqk, dv, int(bool(causal)), _P_MODES[p_mode],
-                          _stream_ptr(stream, q8.device))
+    lse = _lse_out(return_lse, B, Hq, S, q8.device)
+    st = attn_fwd_fp8_lse_raw(q8.data_ptr(), k8.data_ptr(), v8.data_ptr(), out.data_ptr(),
+                              0 if lse is None else lse.data_ptr(),
+                              float(q_scale), float(k_scale), float(v_scale), sm,
+                              B, Hq, Hkv, S, dqk, dv, int(bool(causal)), _P_MODES[p_mode],
+                              _stream_ptr(stream, q8.device))
     _check(st)
-    return out
+    return (out, lse) if return_lse else out
 
 
-def attn_fwd_bf16(q, k, v, softmax_scale=None, causal=True, out=None, stream=None):
-    """Causal BF16 attention on bf16 (B,S,H,d) tensors; returns bf16 (B,S,Hq,d_v)."""
+def attn_fwd_bf16(q, k, v, softmax_scale=None, causal=True, out=None, stream=None, return_lse=False):
+    """BF16 attention (causal by default) on bf16 (B,S,H,d) tensors; returns bf16 (B,S,Hq,d_v),
+    or (out, lse) with ``return_lse`` (lse fp32 (B, Hq, S))."""
     for t, n in ((q, "q"), (k, "k"), (v, "v")):
         if t.dtype != torch.bfloat16:
             raise TypeError(f"{n} must be bfloat16, got {t.dtype}")
@@ -164,10 +190,12 @@ def attn_fwd_bf16(q, k, v, softmax_scale=None, causal=True, out=None, stream=Non
     elif out.dtype != torch.bfloat16 or tuple(out.shape) != (B, S, Hq, dv) or not out.is_contiguous():
         raise ValueError("out must be a contiguous bf16 tensor of shape (B, S, Hq, d_v)")
     sm = 0.0 if softmax_scale is None else float(softmax_scale)
-    st = attn_fwd_bf16_raw(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), sm,
-                           B, Hq, Hkv, S, dqk, dv, int(bool(causal)), _stream_ptr(stream, q.device))
+    lse = _lse_out(return_lse, B, Hq, S, q.device)
+    st = attn_fwd_bf16_lse_raw(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                               0 if lse is None else lse.data_ptr(), sm,
+                               B, Hq, Hkv, S, dqk, dv, int(bool(causal)), _stream_ptr(stream, q.device))
     _check(st)
-    return out
+    return (out, lse) if return_lse else out
 
 
 def causal_flops(B, Hq, S, d_qk, d_v):

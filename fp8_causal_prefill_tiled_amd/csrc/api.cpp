@@ -29,9 +29,9 @@ bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
 
 // Shared checks; elem_qkv = bytes per Q/K/V element.  Returns ATTN_OK, an error,
 // or -1 for "empty problem, nothing to do".
-int check_common(const void* q, const void* k, const void* v, void* o, float softmax_scale,
-                 int B, int Hq, int Hkv, int S, int d_qk, int d_v, int causal, size_t elem_qkv,
-                 const char* who) {
+int check_common(const void* q, const void* k, const void* v, void* o, const float* lse,
+                 float softmax_scale, int B, int Hq, int Hkv, int S, int d_qk, int d_v, int causal,
+                 size_t elem_qkv, const char* who) {
     if (B < 0 || S < 0) return fail(ATTN_E_INVALID_ARG, "%s: B=%d and S=%d must be >= 0", who, B, S);
     if (Hq <= 0 || Hkv <= 0) return fail(ATTN_E_INVALID_ARG, "%s: Hq=%d and Hkv=%d must be >= 1", who, Hq, Hkv);
     if (Hq % Hkv != 0) return fail(ATTN_E_INVALID_ARG, "%s: Hq=%d is not a multiple of Hkv=%d", who, Hq, Hkv);
@@ -40,7 +40,6 @@ int check_common(const void* q, const void* k, const void* v, void* o, float sof
     if (causal != 0 && causal != 1) return fail(ATTN_E_INVALID_ARG, "%s: causal=%d must be 0 or 1", who, causal);
     if (d_qk != 128 && d_qk != 192) return fail(ATTN_E_UNSUPPORTED, "%s: d_qk=%d unsupported (128 or 192)", who, d_qk);
     if (d_v != 128) return fail(ATTN_E_UNSUPPORTED, "%s: d_v=%d unsupported (128)", who, d_v);
-    if (causal != 1) return fail(ATTN_E_UNSUPPORTED, "%s: only causal attention is implemented", who);
     // Every element offset is formed in 64-bit arithmetic by the kernels; the row
     // index b*S+s and the head count must fit comfortably in 32-bit integers.
     if ((int64_t)B * S > (int64_t)1 << 30) return fail(ATTN_E_UNSUPPORTED, "%s: B*S=%lld too large", who, (long long)B * S);
@@ -54,6 +53,13 @@ int check_common(const void* q, const void* k, const void* v, void* o, float sof
     const size_t no = (size_t)B * S * Hq * d_v * 2;
     if (overlaps(o, no, q, nq) || overlaps(o, no, k, nk) || overlaps(o, no, v, nv))
         return fail(ATTN_E_INVALID_ARG, "%s: output overlaps an input", who);
+    if (lse) {
+        if ((reinterpret_cast<uintptr_t>(lse) & 3u) != 0)
+            return fail(ATTN_E_INVALID_ARG, "%s: lse pointer must be 4-byte aligned", who);
+        const size_t nl = (size_t)B * Hq * S * sizeof(float);
+        if (overlaps(lse, nl, q, nq) || overlaps(lse, nl, k, nk) || overlaps(lse, nl, v, nv) || overlaps(lse, nl, o, no))
+            return fail(ATTN_E_INVALID_ARG, "%s: lse overlaps another tensor", who);
+    }
     return ATTN_OK;
 }
 
@@ -67,12 +73,12 @@ int finish(hipError_t e, const char* who) {
 
 extern "C" {
 
-int attn_fwd_fp8(const void* q, const void* k, const void* v, void* o,
-                 float q_scale, float k_scale, float v_scale, float softmax_scale,
-                 int B, int Hq, int Hkv, int S, int d_qk, int d_v,
-                 int causal, int p_mode, hipStream_t stream) {
-    const char* who = "attn_fwd_fp8";
-    int st = check_common(q, k, v, o, softmax_scale, B, Hq, Hkv, S, d_qk, d_v, causal, 1, who);
+int attn_fwd_fp8_lse(const void* q, const void* k, const void* v, void* o, float* lse,
+                     float q_scale, float k_scale, float v_scale, float softmax_scale,
+                     int B, int Hq, int Hkv, int S, int d_qk, int d_v,
+                     int causal, int p_mode, hipStream_t stream) {
+    const char* who = lse ? "attn_fwd_fp8_lse" : "attn_fwd_fp8";
+    int st = check_common(q, k, v, o, lse, softmax_scale, B, Hq, Hkv, S, d_qk, d_v, causal, 1, who);
     if (st == -1) { g_err[0] = 0; return ATTN_OK; }
     if (st != ATTN_OK) return st;
     if (!(std::isfinite(q_scale) && q_scale > 0.f) || !(std::isfinite(k_scale) && k_scale > 0.f) ||
@@ -82,22 +88,35 @@ int attn_fwd_fp8(const void* q, const void* k, const void* v, void* o,
         return fail(ATTN_E_INVALID_ARG, "%s: p_mode=%d must be 0 (exact) or 1 (lean)", who, p_mode);
     attnfwd::Problem p{q, k, v, o, q_scale, k_scale, v_scale,
                        softmax_scale > 0.f ? softmax_scale : 1.0f / std::sqrt((float)d_qk),
-                       B, Hq, Hkv, S, d_qk, d_v, p_mode, stream};
+                       B, Hq, Hkv, S, d_qk, d_v, p_mode, stream, lse, causal};
     const double c = (double)q_scale * k_scale * p.sm * 1.4426950408889634;
     if (!(c < 1e30 && c > 1e-30)) return fail(ATTN_E_INVALID_ARG, "%s: q_scale*k_scale*softmax_scale out of range", who);
     return finish(attnfwd::launch_fp8(p), who);
 }
 
-int attn_fwd_bf16(const void* q, const void* k, const void* v, void* o, float softmax_scale,
-                  int B, int Hq, int Hkv, int S, int d_qk, int d_v, int causal, hipStream_t stream) {
-    const char* who = "attn_fwd_bf16";
-    int st = check_common(q, k, v, o, softmax_scale, B, Hq, Hkv, S, d_qk, d_v, causal, 2, who);
+int attn_fwd_fp8(const void* q, const void* k, const void* v, void* o,
+                 float q_scale, float k_scale, float v_scale, float softmax_scale,
+                 int B, int Hq, int Hkv, int S, int d_qk, int d_v,
+                 int causal, int p_mode, hipStream_t stream) {
+    return attn_fwd_fp8_lse(q, k, v, o, nullptr, q_scale, k_scale, v_scale, softmax_scale,
+                            B, Hq, Hkv, S, d_qk, d_v, causal, p_mode, stream);
+}
+
+int attn_fwd_bf16_lse(const void* q, const void* k, const void* v, void* o, float* lse, float softmax_scale,
+                      int B, int Hq, int Hkv, int S, int d_qk, int d_v, int causal, hipStream_t stream) {
+    const char* who = lse ? "attn_fwd_bf16_lse" : "attn_fwd_bf16";
+    int st = check_common(q, k, v, o, lse, softmax_scale, B, Hq, Hkv, S, d_qk, d_v, causal, 2, who);
     if (st == -1) { g_err[0] = 0; return ATTN_OK; }
     if (st != ATTN_OK) return st;
     attnfwd::Problem p{q, k, v, o, 1.f, 1.f, 1.f,
                        softmax_scale > 0.f ? softmax_scale : 1.0f / std::sqrt((float)d_qk),
-                       B, Hq, Hkv, S, d_qk, d_v, 0, stream};
+                       B, Hq, Hkv, S, d_qk, d_v, 0, stream, lse, causal};
     return finish(attnfwd::launch_bf16(p), who);
+}
+
+int attn_fwd_bf16(const void* q, const void* k, const void* v, void* o, float softmax_scale,
+                  int B, int Hq, int Hkv, int S, int d_qk, int d_v, int causal, hipStream_t stream) {
+    return attn_fwd_bf16_lse(q, k, v, o, nullptr, softmax_scale, B, Hq, Hkv, S, d_qk, d_v, causal, stream);
 }
 
 int attn_rotate_quant_bf16(const void* x, void* x8, float* scale, int B, int S, int H, int d,
@@ -120,6 +139,6 @@ int attn_rotate_quant_bf16(const void* x, void* x8, float* scale, int B, int S, 
 
 const char* attn_last_error(void) { return g_err; }
 
-int attn_abi_version(void) { return 100; }
+int attn_abi_version(void) { return 101; }
 
 }  // extern "C"

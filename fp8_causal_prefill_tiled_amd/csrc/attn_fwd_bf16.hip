@@ -62,7 +62,8 @@ struct Bf16Params {
     const __bf16* k;
     const __bf16* v;
     __bf16* o;
-    float c;   // sm * log2(e)
+    float* lse;   // (B, Hq, S) natural-log normaliser per query row, or null
+    float c;      // sm * log2(e)
     int B, Hq, Hkv, S;
     int n_tiles;
 };
@@ -79,7 +80,7 @@ __device__ __forceinline__ void mfma_bf16_vacc(f32x16& acc, const bf16x8& a, con
     asm("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(acc) : "v"(a), "v"(b));
 }
 
-template <int DQK>
+template <int DQK, bool CAUSAL, bool LSE>
 __global__ void __launch_bounds__(512) bf16_causal_fwd(Bf16Params a) {
     using T = Bf16Tile<DQK>;
     constexpr int NT = 256;                       // threads per group
@@ -99,16 +100,17 @@ __global__ void __launch_bounds__(512) bf16_causal_fwd(Bf16Params a) {
     const int tg = tid & (NT - 1);                            // thread index in its group
     const int BH = a.B * a.Hq;
     const int L = blockIdx.x;
-    const int tile = a.n_tiles - 1 - L / BH;      // heaviest (longest causal prefix) tiles first
+    const int tile = a.n_tiles - 1 - L / BH;      // heaviest (longest causal prefix) tiles first when causal
     const int bh = L % BH;                        // consecutive blocks: consecutive heads (XCD spread)
     const int b = bh / a.Hq;
     const int h = bh - b * a.Hq;
     const int g = h / (a.Hq / a.Hkv);
     const int S = a.S;
     const int q0 = tile * BM;
-    const int kend = min(S, q0 + BM);
+    const int kend = CAUSAL ? min(S, q0 + BM) : S;
     const int nblk = (kend + KB - 1) / KB;        // key blocks the workgroup walks
-    const int jdiag = q0 / KB;                    // first block that needs the causal mask
+    // first block that needs a mask: the diagonal one (causal) or the ragged last one
+    const int jdiag = CAUSAL ? q0 / KB : (S - 1) / KB;
 
     const int c = lane & 31;
     const int hh = lane >> 5;
@@ -241,8 +243,10 @@ __global__ void __launch_bounds__(512) bf16_causal_fwd(Bf16Params a) {
     float mx_n = -INFINITY;
     auto prep_mask = [&](int j) {
         if (j >= jdiag) {
-            // key kb0 + off(r) + 4hh is visible iff off(r) <= min(qabs, S-1) - kb0 - 4hh
-            const int lim = min(qabs, S - 1) - j * KB - 4 * hh;
+            // key kb0 + off(r) + 4hh is visible iff off(r) <= qlim - kb0 - 4hh, qlim the
+            // last key the query sees
+            const int qlim = CAUSAL ? min(qabs, S - 1) : S - 1;
+            const int lim = qlim - j * KB - 4 * hh;
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
                 const int off = 8 * (r >> 2) + (r & 3);
@@ -404,8 +408,11 @@ __global__ void __launch_bounds__(512) bf16_causal_fwd(Bf16Params a) {
     // all matrix work (and any operand copies it needs) out of the divergent stores.
     vacc_settle(o);
 
-    // ---- epilogue: out = bf16(O / l), lane holds query c, d = 32dt + 8(r/4) + 4hh + r%4
+    // ---- epilogue: out = bf16(O / l), lane holds query c, d = 32dt + 8(r/4) + 4hh + r%4.
+    // l = sum_j 2^(t_j - ref), so the row's natural-log normaliser is ln2 * (log2 l + ref).
     const float lsum = lpart + other_half(lpart);
+    if (LSE && hh == 0 && qabs < S)
+        a.lse[((int64_t)b * a.Hq + h) * S + qabs] = (log2f(lsum) + ref) * 0.6931471805599453f;
     if (qabs < S) {
         __bf16* op = a.o + (((int64_t)b * S + qabs) * a.Hq + h) * 128;
 #pragma unroll
@@ -423,7 +430,7 @@ __global__ void __launch_bounds__(512) bf16_causal_fwd(Bf16Params a) {
     }
 }
 
-template <int DQK>
+template <int DQK, bool CAUSAL, bool LSE>
 hipError_t launch_t(const Problem& p) {
     constexpr int BM = 256;
     Bf16Params a;
@@ -431,6 +438,7 @@ hipError_t launch_t(const Problem& p) {
     a.k = static_cast<const __bf16*>(p.k);
     a.v = static_cast<const __bf16*>(p.v);
     a.o = static_cast<__bf16*>(p.o);
+    a.lse = p.lse;
     a.c = (float)((double)p.sm * 1.4426950408889634);
     a.B = p.B;
     a.Hq = p.Hq;
@@ -439,16 +447,24 @@ hipError_t launch_t(const Problem& p) {
     a.n_tiles = (p.S + BM - 1) / BM;
     const long long nblocks = (long long)a.n_tiles * p.B * p.Hq;
     if (nblocks <= 0 || nblocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-    hipLaunchKernelGGL((bf16_causal_fwd<DQK>), dim3((unsigned)nblocks), dim3(512), 0, p.stream, a);
+    hipLaunchKernelGGL((bf16_causal_fwd<DQK, CAUSAL, LSE>), dim3((unsigned)nblocks), dim3(512), 0, p.stream, a);
     return hipGetLastError();
+}
+
+// The log-sum-exp store is a template switch: the kernels without it keep exactly the
+// code they have when no caller asks for it.
+template <bool CAUSAL, bool LSE>
+hipError_t launch_c(const Problem& p) {
+    if (p.d_qk == 128) return launch_t<128, CAUSAL, LSE>(p);
+    if (p.d_qk == 192) return launch_t<192, CAUSAL, LSE>(p);
+    return hipErrorInvalidValue;
 }
 
 }  // namespace
 
 hipError_t launch_bf16(const Problem& p) {
-    if (p.d_qk == 128) return launch_t<128>(p);
-    if (p.d_qk == 192) return launch_t<192>(p);
-    return hipErrorInvalidValue;
+    if (p.lse) return p.causal ? launch_c<true, true>(p) : launch_c<false, true>(p);
+    return p.causal ? launch_c<true, false>(p) : launch_c<false, false>(p);
 }
 
 }  // namespace attnfwd

@@ -54,6 +54,7 @@ struct Fp8Params {
     const uint8_t* k;
     const uint8_t* v;
     __bf16* o;
+    float* lse;     // (B, Hq, S) natural-log normaliser per query row, or null
     float c;        // q_scale * k_scale * sm * log2(e)
     float a8;       // 8 * c, the Lean-P slope
     float v_scale;
@@ -95,7 +96,7 @@ __device__ __forceinline__ int v_swz(int row) { return (row & 3) | (((row >> 3) 
 // workgroup with the transposing ds_read_b64_tr_b8, far slower per byte than
 // ds_read_b128 on gfx950.  Buffer loads use a range ending at row S, so rows
 // past S read as zeros.
-template <int DQK, int PMODE>
+template <int DQK, int PMODE, bool CAUSAL, bool LSE>
 __global__ void __launch_bounds__(512) fp8_causal_fwd(Fp8Params a) {
     using T = Fp8Tile<DQK>;
     constexpr int NT = 256;                       // threads per group
@@ -117,16 +118,17 @@ __global__ void __launch_bounds__(512) fp8_causal_fwd(Fp8Params a) {
     const int tg = tid & (NT - 1);                            // thread index in its group
     const int BH = a.B * a.Hq;
     const int L = blockIdx.x;
-    const int tile = a.n_tiles - 1 - L / BH;      // heaviest (longest causal prefix) tiles first
+    const int tile = a.n_tiles - 1 - L / BH;      // heaviest (longest causal prefix) tiles first when causal
     const int bh = L % BH;                        // consecutive blocks: consecutive heads (XCD spread)
     const int b = bh / a.Hq;
     const int h = bh - b * a.Hq;
     const int g = h / (a.Hq / a.Hkv);
     const int S = a.S;
     const int q0 = tile * BM;
-    const int kend = min(S, q0 + BM);
+    const int kend = CAUSAL ? min(S, q0 + BM) : S;
     const int nblk = (kend + KB - 1) / KB;        // key blocks the workgroup walks
-    const int jdiag = q0 / KB;                    // first block that needs the causal mask
+    // first block that needs a mask: the diagonal one (causal) or the ragged last one
+    const int jdiag = CAUSAL ? q0 / KB : (S - 1) / KB;
 
     const int c = lane & 31;
     const int hh = lane >> 5;
@@ -279,8 +281,10 @@ __global__ void __launch_bounds__(512) fp8_causal_fwd(Fp8Params a) {
     int sb_n = 127;
     auto prep_mask = [&](int j) {
         if (j >= jdiag) {
-            // key kb0 + off(r) + 4hh is visible iff off(r) <= min(qabs, S-1) - kb0 - 4hh
-            const int lim = min(qabs, S - 1) - j * KB - 4 * hh;
+            // key kb0 + off(r) + 4hh is visible iff off(r) <= qlim - kb0 - 4hh, qlim the
+            // last key the query sees
+            const int qlim = CAUSAL ? min(qabs, S - 1) : S - 1;
+            const int lim = qlim - j * KB - 4 * hh;
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
                 const int off = 8 * (r >> 2) + (r & 3);
@@ -455,9 +459,12 @@ __global__ void __launch_bounds__(512) fp8_causal_fwd(Fp8Params a) {
     vacc_settle(o, lsum);
 
     // ---- epilogue: out = bf16(v_scale * (O / L)), lane holds query c,
-    // d = 32dt + 8(r/4) + 4hh + r%4
+    // d = 32dt + 8(r/4) + 4hh + r%4.  L = sum_j 2^(t_j - ref) over the rounded
+    // probabilities, so the row's natural-log normaliser is ln2 * (log2 L + ref).
+    const float l0 = lsum[0];
+    if (LSE && hh == 0 && qabs < S)
+        a.lse[((int64_t)b * a.Hq + h) * S + qabs] = (log2f(l0) + ref) * 0.6931471805599453f;
     if (qabs < S) {
-        const float l0 = lsum[0];
         __bf16* op = a.o + (((int64_t)b * S + qabs) * a.Hq + h) * 128;
 #pragma unroll
         for (int dt = 0; dt < 4; ++dt) {
@@ -474,7 +481,7 @@ __global__ void __launch_bounds__(512) fp8_causal_fwd(Fp8Params a) {
     }
 }
 
-template <int DQK, int PMODE>
+template <int DQK, int PMODE, bool CAUSAL, bool LSE>
 hipError_t launch_t(const Problem& p) {
     constexpr int NW = 8;
     constexpr int BM = 256;
@@ -483,6 +490,7 @@ hipError_t launch_t(const Problem& p) {
     a.k = static_cast<const uint8_t*>(p.k);
     a.v = static_cast<const uint8_t*>(p.v);
     a.o = static_cast<__bf16*>(p.o);
+    a.lse = p.lse;
     const double c = (double)p.q_scale * p.k_scale * p.sm * 1.4426950408889634;
     a.c = (float)c;
     a.a8 = (float)(8.0 * c);
@@ -494,16 +502,24 @@ hipError_t launch_t(const Problem& p) {
     a.n_tiles = (p.S + BM - 1) / BM;
     const long long nblocks = (long long)a.n_tiles * p.B * p.Hq;
     if (nblocks <= 0 || nblocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-    hipLaunchKernelGGL((fp8_causal_fwd<DQK, PMODE>), dim3((unsigned)nblocks), dim3(NW * 64), 0, p.stream, a);
+    hipLaunchKernelGGL((fp8_causal_fwd<DQK, PMODE, CAUSAL, LSE>), dim3((unsigned)nblocks), dim3(NW * 64), 0, p.stream, a);
     return hipGetLastError();
+}
+
+// The log-sum-exp store is a template switch: the kernels without it keep exactly the
+// code (and code layout) they have when no caller asks for it.
+template <bool CAUSAL, bool LSE>
+hipError_t launch_c(const Problem& p) {
+    if (p.d_qk == 128) return p.p_mode == 0 ? launch_t<128, 0, CAUSAL, LSE>(p) : launch_t<128, 1, CAUSAL, LSE>(p);
+    if (p.d_qk == 192) return p.p_mode == 0 ? launch_t<192, 0, CAUSAL, LSE>(p) : launch_t<192, 1, CAUSAL, LSE>(p);
+    return hipErrorInvalidValue;
 }
 
 }  // namespace
 
 hipError_t launch_fp8(const Problem& p) {
-    if (p.d_qk == 128) return p.p_mode == 0 ? launch_t<128, 0>(p) : launch_t<128, 1>(p);
-    if (p.d_qk == 192) return p.p_mode == 0 ? launch_t<192, 0>(p) : launch_t<192, 1>(p);
-    return hipErrorInvalidValue;
+    if (p.lse) return p.causal ? launch_c<true, true>(p) : launch_c<false, true>(p);
+    return p.causal ? launch_c<true, false>(p) : launch_c<false, false>(p);
 }
 
 }  // namespace attnfwd

@@ -16,6 +16,8 @@ struct Problem {
     int B, Hq, Hkv, S, d_qk, d_v;
     int p_mode;
     hipStream_t stream;
+    float* lse;   // (B, Hq, S) fp32 per-row log-sum-exp output, or null
+    int causal;   // 1: key j visible to query i iff j <= i; 0: every key visible
 };
 
 hipError_t launch_fp8(const Problem& p);

@@ -2,14 +2,15 @@
  * attn_fwd.h - C ABI of libattnfwd.so: causal forward prefill attention on
  * AMD Instinct MI355X (CDNA4, gfx950).
  *
- * Operation (both entry points): for every batch b, query head h and query
- * position i < S,
+ * Operation (every attention entry point): for every batch b, query head h and
+ * query position i < S,
  *
- *     O[b,i,h,:] = sum_{j<=i} softmax_j( sm * <Q[b,i,h,:], K[b,j,g,:]> ) * V[b,j,g,:]
+ *     O[b,i,h,:] = sum_{j in K(i)} softmax_j( sm * <Q[b,i,h,:], K[b,j,g,:]> ) * V[b,j,g,:]
  *
- * with g = h / (Hq / Hkv) (grouped-query attention by consecutive groups) and
- * sm the softmax scale.  This is the causal, equal-length forward prefill the
- * pages scope the kernels to ("Breaking the FP8 Attention Bottleneck on AMD
+ * with g = h / (Hq / Hkv) (grouped-query attention by consecutive groups), sm
+ * the softmax scale and K(i) the keys query i sees: j <= i when causal == 1,
+ * every j < S when causal == 0.  The causal case is the equal-length forward
+ * prefill the pages scope the kernels to ("Breaking the FP8 Attention Bottleneck on AMD
  * MI355X: How Zyphra ZYFA Unleashes Performance", section "Application
  * Boundaries and Engineering Decisions"; "Zyphra ZYFA: FP8 FlashAttention for
  * AMD MI355X, Up to 1.76x Faster", TL;DR and comparison table row "Scope"),
@@ -25,9 +26,13 @@
  * returns without synchronising; O is valid once the stream has completed.
  * O must not overlap Q, K or V.
  *
+ * The non-causal case (causal == 0) is the same loop over every key block, with
+ * only the ragged last block masked.
+ *
  * Supported shapes: d_qk in {128, 192}, d_v == 128, Hq % Hkv == 0, S >= 1
- * (any S; the ragged last tile is masked), causal == 1, pointers 16-byte
- * aligned.  B == 0 or S == 0 is an empty problem: ATTN_OK, nothing launched.
+ * (any S; the ragged last tile is masked), causal in {0, 1}, tensor pointers
+ * 16-byte aligned.  B == 0 or S == 0 is an empty problem: ATTN_OK, nothing
+ * launched.
  *
  * Errors: every argument check happens on the host before any HIP call and
  * returns ATTN_E_INVALID_ARG (a malformed argument) or ATTN_E_UNSUPPORTED (a
@@ -87,6 +92,30 @@ int attn_fwd_fp8(const void* q, const void* k, const void* v, void* o,
                  int causal, int p_mode, hipStream_t stream);
 
 /*
+ * attn_fwd_fp8 that also writes the log-sum-exp of every query row.
+ *
+ * lse: device pointer to B*Hq*S floats, layout (B, Hq, S) contiguous, 4-byte
+ *      aligned, owned by the caller, not overlapping q, k, v or o; NULL makes
+ *      the call identical to attn_fwd_fp8.  lse[b,h,i] = ln sum_{j in K(i)}
+ *      exp(sm * <q_i, k_j>) on the dequantised inputs, taken from the very
+ *      normaliser the kernel divides by: the sum of the rounded e4m3
+ *      probabilities times their block powers of two.  It therefore carries the
+ *      probability rounding: |lse - exact| <= ln(1 + 2^-4) per row on the exact
+ *      path (each e4m3 rounding moves a term by at most 2^-4 of itself), and
+ *      within the Lean-P code law's ratio range (the linear-mantissa chord
+ *      overstates 2^x by at most 6.2%, plus half a code step) on Lean P.
+ *      (B, Hq, S) is the layout FlashAttention-style libraries return it in;
+ *      with O it is what exact merging of partial attention over key subsets
+ *      needs (two partial results combine as a softmax over their lse values).
+ * Other arguments, behaviour and errors as attn_fwd_fp8; a misaligned or
+ * overlapping lse is ATTN_E_INVALID_ARG.
+ */
+int attn_fwd_fp8_lse(const void* q, const void* k, const void* v, void* o, float* lse,
+                     float q_scale, float k_scale, float v_scale, float softmax_scale,
+                     int B, int Hq, int Hkv, int S, int d_qk, int d_v,
+                     int causal, int p_mode, hipStream_t stream);
+
+/*
  * BF16 causal prefill attention (the BF16 kernel of "Zyphra ZYFA: FP8
  * FlashAttention...", section "What is ZYFA?").
  *
@@ -100,6 +129,17 @@ int attn_fwd_bf16(const void* q, const void* k, const void* v, void* o,
                   float softmax_scale,
                   int B, int Hq, int Hkv, int S, int d_qk, int d_v,
                   int causal, hipStream_t stream);
+
+/*
+ * attn_fwd_bf16 that also writes the log-sum-exp of every query row: lse as
+ * for attn_fwd_fp8_lse (B*Hq*S floats, (B, Hq, S), NULL = none), here from the
+ * fp32 sum of the unrounded probabilities, so it matches the exact value on
+ * the bf16 inputs to fp32 accuracy.
+ */
+int attn_fwd_bf16_lse(const void* q, const void* k, const void* v, void* o, float* lse,
+                      float softmax_scale,
+                      int B, int Hq, int Hkv, int S, int d_qk, int d_v,
+                      int causal, hipStream_t stream);
 
 /*
  * Hadamard rotation and per-tensor FP8 quantisation of a Q or K tensor ("Zyphra

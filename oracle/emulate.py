@@ -87,8 +87,10 @@ def emulate_fp8(q8, k8, v8, q_scale, k_scale, v_scale, sm_scale=None, p_mode="ex
     """Emulate the FP8 method on e4m3 codes (uint8 arrays, (B, S, H, d) layout).
 
     Returns O (B, len(rows), Hq, d_v) float64.  With ``return_lse`` also returns
-    the per-row natural-log normaliser of the *rounded* weights,
-    ln(sum_b 2^(M_ib-8) l_ib) / ... expressed as log2: log2L (B, len(rows), Hq).
+    log2L (B, len(rows), Hq) = log2(sum_b 2^(M_ib - 8) l_ib), the base-2 log of the
+    denominator step 6 divides by (the sum of the rounded probabilities, each block
+    at its own power of two).  Without rounding it is log2 sum_j 2^(t_ij), so
+    ln(2) * log2L is the row's log-sum-exp of the logits sm * <q_i, k_j>.
     """
     q8 = np.asarray(q8, dtype=np.uint8)
     k8 = np.asarray(k8, dtype=np.uint8)

@@ -23,7 +23,7 @@ import torch
 
 from fp8_causal_prefill_tiled_amd import binding
 from fp8_causal_prefill_tiled_amd import workloads as W
-from oracle.attention64 import attention_fp64, dequantize, rel_rms
+from oracle.attention64 import attention_fp64, dequantize, lse_fp64, rel_rms
 from oracle.emulate import emulate_fp8
 from oracle.e4m3 import bf16_rne, decode_e4m3
 
@@ -35,43 +35,61 @@ def tol_fp64(emu_err):
     return max(2e-2, 1.1 * emu_err + 2e-3)
 
 
-def run_fp8(d, mode, dev="cuda:0"):
+def run_fp8(d, mode, dev="cuda:0", causal=True, return_lse=False):
     q8, k8, v8 = (d[n].to(dev) for n in ("q8", "k8", "v8"))
-    out = binding.attn_fwd_fp8(q8, k8, v8, d["q_scale"], d["k_scale"], d["v_scale"], p_mode=mode)
+    out = binding.attn_fwd_fp8(q8, k8, v8, d["q_scale"], d["k_scale"], d["v_scale"], p_mode=mode,
+                               causal=causal, return_lse=return_lse)
     torch.cuda.synchronize()
     return out
 
 
-def run_bf16(d, dev="cuda:0"):
+def run_bf16(d, dev="cuda:0", causal=True, return_lse=False):
     q, k, v = (d[n].to(dev) for n in ("q", "k", "v"))
-    out = binding.attn_fwd_bf16(q, k, v)
+    out = binding.attn_fwd_bf16(q, k, v, causal=causal, return_lse=return_lse)
     torch.cuda.synchronize()
     return out
 
 
-def oracle_fp8(d, mode, heads=None, rows=None):
-    """(emulation, fp64) for the given query heads and rows; arrays (B, rows, heads, d_v)."""
+def oracle_fp8(d, mode, heads=None, rows=None, causal=True, with_lse=False):
+    """(emulation, fp64) for the given query heads and rows; arrays (B, rows, heads, d_v).
+
+    With ``with_lse`` also (emulated, fp64) natural-log normalisers, arrays (B, heads, rows)."""
     q8, k8, v8 = d["q8"].numpy(), d["k8"].numpy(), d["v8"].numpy()
     Hq, Hkv = q8.shape[2], k8.shape[2]
     heads = list(range(Hq)) if heads is None else list(heads)
-    emus, refs = [], []
+    emus, refs, lemus, lrefs = [], [], [], []
     for h in heads:
         g = h // (Hq // Hkv)
         qs, ks, vs = q8[:, :, h:h + 1], k8[:, :, g:g + 1], v8[:, :, g:g + 1]
-        emus.append(emulate_fp8(qs, ks, vs, d["q_scale"], d["k_scale"], d["v_scale"], p_mode=mode, rows=rows))
+        e = emulate_fp8(qs, ks, vs, d["q_scale"], d["k_scale"], d["v_scale"], p_mode=mode, rows=rows,
+                        causal=causal, return_lse=with_lse)
+        if with_lse:
+            e, log2L = e
+            lemus.append(np.log(2.0) * log2L.transpose(0, 2, 1))
+            lrefs.append(lse_fp64(dequantize(qs, d["q_scale"]), dequantize(ks, d["k_scale"]), rows=rows,
+                                  causal=causal))
+        emus.append(e)
         refs.append(attention_fp64(dequantize(qs, d["q_scale"]), dequantize(ks, d["k_scale"]),
-                                   dequantize(vs, d["v_scale"]), rows=rows))
-    return np.concatenate(emus, axis=2), np.concatenate(refs, axis=2)
+                                   dequantize(vs, d["v_scale"]), rows=rows, causal=causal))
+    res = (np.concatenate(emus, axis=2), np.concatenate(refs, axis=2))
+    if with_lse:
+        res += (np.concatenate(lemus, axis=1), np.concatenate(lrefs, axis=1))
+    return res
 
 
-def oracle_bf16(d, heads=None, rows=None):
+def oracle_bf16(d, heads=None, rows=None, causal=True, with_lse=False):
     q, k, v = (d[n].float().numpy() for n in ("q", "k", "v"))
     Hq, Hkv = q.shape[2], k.shape[2]
     heads = list(range(Hq)) if heads is None else list(heads)
-    refs = []
+    refs, lrefs = [], []
     for h in heads:
         g = h // (Hq // Hkv)
-        refs.append(attention_fp64(q[:, :, h:h + 1], k[:, :, g:g + 1], v[:, :, g:g + 1], rows=rows))
+        refs.append(attention_fp64(q[:, :, h:h + 1], k[:, :, g:g + 1], v[:, :, g:g + 1], rows=rows,
+                                   causal=causal))
+        if with_lse:
+            lrefs.append(lse_fp64(q[:, :, h:h + 1], k[:, :, g:g + 1], rows=rows, causal=causal))
+    if with_lse:
+        return np.concatenate(refs, axis=2), np.concatenate(lrefs, axis=1)
     return np.concatenate(refs, axis=2)
 
 

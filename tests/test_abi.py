@@ -33,9 +33,10 @@ def declared_functions():
 
 def test_exports_every_declared_symbol(lib):
     decl = declared_functions()
-    assert {"attn_fwd_fp8", "attn_fwd_bf16", "attn_last_error", "attn_abi_version"} <= decl
+    assert {"attn_fwd_fp8", "attn_fwd_fp8_lse", "attn_fwd_bf16", "attn_fwd_bf16_lse", "attn_last_error",
+            "attn_abi_version"} <= decl
     assert decl <= binding.exported_symbols()
-    assert lib.attn_abi_version() == 100
+    assert lib.attn_abi_version() == 101
 
 
 # fake, never-dereferenced, 16-byte aligned device addresses of disjoint buffers
@@ -59,7 +60,7 @@ def bf16(**kw):
     (dict(q=0), INVALID), (dict(o=0), INVALID), (dict(v=0), INVALID),
     (dict(Hq=3), INVALID), (dict(Hkv=0), INVALID), (dict(S=-1), INVALID), (dict(B=-2), INVALID),
     (dict(d_qk=64), UNSUPPORTED), (dict(d_qk=0), INVALID), (dict(d_v=192), UNSUPPORTED),
-    (dict(causal=0), UNSUPPORTED), (dict(causal=2), INVALID),
+    (dict(causal=-1), INVALID), (dict(causal=2), INVALID),
     (dict(p_mode=2), INVALID), (dict(p_mode=-1), INVALID),
     (dict(q_scale=0.0), INVALID), (dict(k_scale=-1.0), INVALID), (dict(v_scale=math.nan), INVALID),
     (dict(v_scale=math.inf), INVALID), (dict(softmax_scale=math.nan), INVALID),
@@ -78,7 +79,7 @@ def test_fp8_host_validation(lib, kw, status):
 
 @pytest.mark.parametrize("kw,status", [
     (dict(k=0), INVALID), (dict(Hq=5, Hkv=2), INVALID), (dict(d_qk=256), UNSUPPORTED),
-    (dict(causal=0), UNSUPPORTED), (dict(softmax_scale=math.inf), INVALID), (dict(k=K + 1), INVALID),
+    (dict(causal=3), INVALID), (dict(softmax_scale=math.inf), INVALID), (dict(k=K + 1), INVALID),
     (dict(o=V + 64), INVALID), (dict(S=0, q=0, k=0, v=0, o=0), OK),
 ])
 def test_bf16_host_validation(lib, kw, status):
@@ -95,6 +96,35 @@ def test_python_binding_rejects_bad_tensors(lib):
         binding.attn_fwd_fp8(x.float(), x, x, 1.0, 1.0, 1.0)
     with pytest.raises(TypeError):
         binding.attn_fwd_bf16(x, x, x)
+
+
+LSE = 0x50000000
+
+
+@pytest.mark.parametrize("entry", ["fp8", "bf16"])
+@pytest.mark.parametrize("kw,status", [
+    (dict(lse=LSE + 2), INVALID),                 # misaligned
+    (dict(lse=Q + 1024), INVALID),                # inside Q
+    (dict(lse=O + 64), INVALID),                  # inside O
+    (dict(lse=LSE, d_qk=64), UNSUPPORTED),
+    (dict(lse=LSE, S=0, q=0, k=0, v=0, o=0), OK),  # empty: nothing launched
+])
+def test_lse_host_validation(lib, entry, kw, status):
+    if entry == "fp8":
+        a = dict(q=Q, k=K, v=V, o=O, lse=LSE, q_scale=1.0, k_scale=1.0, v_scale=1.0, softmax_scale=0.0,
+                 B=1, Hq=4, Hkv=2, S=128, d_qk=128, d_v=128, causal=0, p_mode=1)
+        a.update(kw)
+        st = binding.attn_fwd_fp8_lse_raw(**a)
+    else:
+        a = dict(q=Q, k=K, v=V, o=O, lse=LSE, softmax_scale=0.0, B=1, Hq=4, Hkv=2, S=128, d_qk=128, d_v=128,
+                 causal=1)
+        a.update(kw)
+        st = binding.attn_fwd_bf16_lse_raw(**a)
+    assert st == status
+    msg = binding.attn_last_error()
+    assert (msg == "") == (status == OK)
+    if status != OK:
+        assert msg.startswith(f"attn_fwd_{entry}_lse")
 
 
 def rotq(**kw):

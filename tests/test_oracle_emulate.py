@@ -11,7 +11,7 @@ and a rounded row sum"; [KG-zh] (Chinese version of the kg.zhiyong.dev article),
 import numpy as np
 import pytest
 
-from oracle.attention64 import attention_fp64, dequantize, rel_rms
+from oracle.attention64 import attention_fp64, dequantize, lse_fp64, rel_rms
 from oracle.e4m3 import decode_e4m3, encode_e4m3_rne
 from oracle.emulate import (emulate_fp8, block_probabilities, encode_probability_lean,
                             encode_probability_exact, LOG2E)
@@ -137,3 +137,32 @@ def test_error_vs_fp64_is_at_the_e4m3_level(p_mode, cap):
     ref = attention_fp64(dequantize(q8, qs), dequantize(k8, ks), dequantize(v8, vs))
     e = rel_rms(emulate_fp8(q8, k8, v8, qs, ks, vs, p_mode=p_mode), ref)
     assert 1e-3 < e < cap
+
+
+# ----------------------------------------------------------------- row log-sum-exp
+
+@pytest.mark.parametrize("causal", [True, False])
+def test_lse_without_rounding_is_the_plain_log_sum_exp(causal):
+    # Special case that reduces to the definition: with the exact path unrounded, the
+    # emulated denominator is sum_j 2^(t_ij), whose log is the fp64 log-sum-exp.
+    q8, k8, v8, qs, ks, vs = _inputs(S=200, Hq=4, Hkv=2, seed=13, sigma_q=2.0)
+    _, log2L = emulate_fp8(q8, k8, v8, qs, ks, vs, rounding=False, causal=causal, return_lse=True, chunk=48)
+    ref = lse_fp64(dequantize(q8, qs), dequantize(k8, ks), causal=causal)      # (B, Hq, S)
+    assert np.max(np.abs(np.log(2.0) * log2L.transpose(0, 2, 1) - ref)) < 1e-12
+
+
+@pytest.mark.parametrize("causal", [True, False])
+@pytest.mark.parametrize("p_mode,lo,hi", [("exact", 1 - 2.0**-4, 1 + 2.0**-4),
+                                          ("lean", 2.0 ** (-1 / 16), 1.0615 * 1.0625)])
+def test_lse_of_rounded_weights_within_the_probability_bounds(p_mode, lo, hi, causal):
+    # The denominator is a sum of rounded probabilities, each within [lo, hi] of its true
+    # value when normal (e4m3 half-ulp on the exact path; chord times half a code step for
+    # Lean P, whose low end is 2^(-1/16): a value just below n + 1/16 rounds down to 2^n).
+    # Values below 2^-6 can be off by all of themselves, but 64 of them weigh less than
+    # 2^-7 of their block's maximum (> 2^7), so the log moves by at most 2^-7 more.
+    q8, k8, v8, qs, ks, vs = _inputs(S=300, Hq=2, Hkv=1, dqk=64, seed=17, sigma_q=2.0)
+    _, log2L = emulate_fp8(q8, k8, v8, qs, ks, vs, p_mode=p_mode, causal=causal, return_lse=True)
+    d = np.log(2.0) * log2L.transpose(0, 2, 1) - lse_fp64(dequantize(q8, qs), dequantize(k8, ks), causal=causal)
+    assert d.min() >= np.log(lo) - 2.0 ** -7 and d.max() <= np.log(hi) + 2.0 ** -7
+    # the rounding is visible (the bound is not vacuous) and mostly averages out over a row
+    assert np.abs(d).max() > 1e-4 and np.abs(d).mean() < 0.05
