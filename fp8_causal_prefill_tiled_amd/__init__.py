@@ -13,6 +13,9 @@ _BINDING_NAMES = {"attn_fwd_fp8", "attn_fwd_bf16", "rotate_quant_bf16", "attn_la
 
 
 def __getattr__(name):
+    if name == "flash_attn_func":
+        from .interface import flash_attn_func
+        return flash_attn_func
     if name in _BINDING_NAMES:
         from . import binding
         return getattr(binding, name)

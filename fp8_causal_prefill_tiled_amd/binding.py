@@ -19,8 +19,8 @@ ATTN_OK, ATTN_E_INVALID_ARG, ATTN_E_UNSUPPORTED, ATTN_E_HIP = 0, 1, 2, 3
 P_EXACT, P_LEAN = 0, 1
 _P_MODES = {"exact": P_EXACT, "lean": P_LEAN, P_EXACT: P_EXACT, P_LEAN: P_LEAN}
 
-_EXPORTS = ("attn_fwd_fp8", "attn_fwd_fp8_lse", "attn_fwd_bf16", "attn_fwd_bf16_lse", "attn_rotate_quant_bf16",
-            "attn_last_error", "attn_abi_version")
+_EXPORTS = ("attn_fwd_fp8", "attn_fwd_fp8_lse", "attn_fwd_fp8_varlen", "attn_fwd_bf16", "attn_fwd_bf16_lse",
+            "attn_fwd_bf16_varlen", "attn_rotate_quant_bf16", "attn_last_error", "attn_abi_version")
 
 
 class AttnError(RuntimeError):
@@ -53,6 +53,10 @@ def load_library():
     lib.attn_fwd_bf16.restype = i
     lib.attn_fwd_bf16_lse.argtypes = [vp, vp, vp, vp, vp, f, i, i, i, i, i, i, i, vp]
     lib.attn_fwd_bf16_lse.restype = i
+    lib.attn_fwd_fp8_varlen.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, f, f, f, f, i, i, i, i, i, i, vp]
+    lib.attn_fwd_fp8_varlen.restype = i
+    lib.attn_fwd_bf16_varlen.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, f, i, i, i, i, i, vp]
+    lib.attn_fwd_bf16_varlen.restype = i
     lib.attn_rotate_quant_bf16.argtypes = [vp, vp, vp, i, i, i, i, vp]
     lib.attn_rotate_quant_bf16.restype = i
     lib.attn_last_error.argtypes = []
@@ -114,6 +118,19 @@ def attn_fwd_bf16_raw(q, k, v, o, softmax_scale, B, Hq, Hkv, S, d_qk, d_v, causa
 def attn_fwd_bf16_lse_raw(q, k, v, o, lse, softmax_scale, B, Hq, Hkv, S, d_qk, d_v, causal, stream=0):
     return load_library().attn_fwd_bf16_lse(q, k, v, o, lse, softmax_scale, B, Hq, Hkv, S, d_qk, d_v, causal,
                                             stream)
+
+
+def attn_fwd_fp8_varlen_raw(q, k, v, o, lse, cu_seqlens, n_seqs, max_seqlen, total_tokens, q_scale, k_scale, v_scale,
+                            softmax_scale, Hq, Hkv, d_qk, d_v, causal, p_mode, stream=0):
+    return load_library().attn_fwd_fp8_varlen(q, k, v, o, lse, cu_seqlens, n_seqs, max_seqlen, total_tokens,
+                                              q_scale, k_scale, v_scale, softmax_scale, Hq, Hkv, d_qk, d_v,
+                                              causal, p_mode, stream)
+
+
+def attn_fwd_bf16_varlen_raw(q, k, v, o, lse, cu_seqlens, n_seqs, max_seqlen, total_tokens, softmax_scale,
+                             Hq, Hkv, d_qk, d_v, causal, stream=0):
+    return load_library().attn_fwd_bf16_varlen(q, k, v, o, lse, cu_seqlens, n_seqs, max_seqlen, total_tokens,
+                                               softmax_scale, Hq, Hkv, d_qk, d_v, causal, stream)
 
 
 def attn_rotate_quant_bf16_raw(x, x8, scale, B, S, H, d, stream=0):
@@ -205,3 +222,64 @@ def causal_flops(B, Hq, S, d_qk, d_v):
 
 def default_softmax_scale(d_qk):
     return 1.0 / math.sqrt(d_qk)
+
+
+def _thd(x, name):
+    if x.dim() != 3:
+        raise ValueError(f"{name} must be (total_tokens, H, d), got shape {tuple(x.shape)}")
+    if not x.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if not x.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    return x.shape
+
+
+def _varlen_common(q, k, v, cu_seqlens, out, return_lse):
+    T, Hq, dqk = _thd(q, "q")
+    Tk, Hkv, dk = _thd(k, "k")
+    Tv, Hv, dv = _thd(v, "v")
+    if (Tk, dk) != (T, dqk) or (Tv, Hv) != (T, Hkv):
+        raise ValueError(f"shape mismatch q{tuple(q.shape)} k{tuple(k.shape)} v{tuple(v.shape)}")
+    if cu_seqlens.dtype != torch.int32 or cu_seqlens.dim() != 1 or not cu_seqlens.is_cuda \
+            or not cu_seqlens.is_contiguous() or cu_seqlens.numel() < 1:
+        raise ValueError("cu_seqlens must be a contiguous 1-D int32 GPU tensor of n_seqs + 1 offsets")
+    if out is None:
+        out = torch.empty((T, Hq, dv), dtype=torch.bfloat16, device=q.device)
+    elif out.dtype != torch.bfloat16 or tuple(out.shape) != (T, Hq, dv) or not out.is_contiguous():
+        raise ValueError("out must be a contiguous bf16 tensor of shape (total_tokens, Hq, d_v)")
+    lse = torch.empty((Hq, T), dtype=torch.float32, device=q.device) if return_lse else None
+    return T, Hq, Hkv, dqk, dv, out, lse
+
+
+def attn_fwd_fp8_varlen(q8, k8, v8, cu_seqlens, max_seqlen, q_scale, k_scale, v_scale, softmax_scale=None,
+                        causal=True, p_mode="exact", out=None, stream=None, return_lse=False):
+    """FP8 attention over a variable-length batch packed along the rows: q8 (total, Hq, d_qk),
+    k8/v8 (total, Hkv, d), sequence i at rows cu_seqlens[i]..cu_seqlens[i+1]-1 (int32 GPU tensor),
+    max_seqlen the longest length (host int).  Returns bf16 (total, Hq, d_v), or (out, lse) with
+    lse fp32 (Hq, total)."""
+    for t, n in ((q8, "q8"), (k8, "k8"), (v8, "v8")):
+        if t.dtype not in (torch.uint8, torch.float8_e4m3fn):
+            raise TypeError(f"{n} must hold e4m3fn bytes (uint8 or float8_e4m3fn), got {t.dtype}")
+    T, Hq, Hkv, dqk, dv, out, lse = _varlen_common(q8, k8, v8, cu_seqlens, out, return_lse)
+    sm = 0.0 if softmax_scale is None else float(softmax_scale)
+    _check(attn_fwd_fp8_varlen_raw(q8.data_ptr(), k8.data_ptr(), v8.data_ptr(), out.data_ptr(),
+                                   0 if lse is None else lse.data_ptr(), cu_seqlens.data_ptr(),
+                                   cu_seqlens.numel() - 1, int(max_seqlen), T, float(q_scale), float(k_scale),
+                                   float(v_scale), sm, Hq, Hkv, dqk, dv, int(bool(causal)), _P_MODES[p_mode],
+                                   _stream_ptr(stream, q8.device)))
+    return (out, lse) if return_lse else out
+
+
+def attn_fwd_bf16_varlen(q, k, v, cu_seqlens, max_seqlen, softmax_scale=None, causal=True, out=None, stream=None,
+                         return_lse=False):
+    """BF16 attention over a variable-length batch (layout as attn_fwd_fp8_varlen)."""
+    for t, n in ((q, "q"), (k, "k"), (v, "v")):
+        if t.dtype != torch.bfloat16:
+            raise TypeError(f"{n} must be bfloat16, got {t.dtype}")
+    T, Hq, Hkv, dqk, dv, out, lse = _varlen_common(q, k, v, cu_seqlens, out, return_lse)
+    sm = 0.0 if softmax_scale is None else float(softmax_scale)
+    _check(attn_fwd_bf16_varlen_raw(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                                    0 if lse is None else lse.data_ptr(), cu_seqlens.data_ptr(),
+                                    cu_seqlens.numel() - 1, int(max_seqlen), T, sm, Hq, Hkv, dqk, dv,
+                                    int(bool(causal)), _stream_ptr(stream, q.device)))
+    return (out, lse) if return_lse else out

@@ -3,6 +3,7 @@
 #include "../../include/attn_fwd.h"
 #include "launch.h"
 
+#include <algorithm>
 #include <cmath>
 #include <cstdarg>
 #include <cstdint>
@@ -27,12 +28,16 @@ bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
     return a0 < b0 + nb && b0 < a0 + na;
 }
 
-// Shared checks; elem_qkv = bytes per Q/K/V element.  Returns ATTN_OK, an error,
-// or -1 for "empty problem, nothing to do".
+// Shared checks; elem_qkv = bytes per Q/K/V element, rows = rows of the tensors
+// (B*S, or the packed total of a variable-length batch).  Returns ATTN_OK, an
+// error, or -1 for "empty problem, nothing to do".
+int finish(hipError_t e, const char* who);
+
 int check_common(const void* q, const void* k, const void* v, void* o, const float* lse,
-                 float softmax_scale, int B, int Hq, int Hkv, int S, int d_qk, int d_v, int causal,
-                 size_t elem_qkv, const char* who) {
+                 float softmax_scale, int B, int Hq, int Hkv, int S, int64_t rows, int d_qk, int d_v,
+                 int causal, size_t elem_qkv, const char* who) {
     if (B < 0 || S < 0) return fail(ATTN_E_INVALID_ARG, "%s: B=%d and S=%d must be >= 0", who, B, S);
+    if (rows < 0) return fail(ATTN_E_INVALID_ARG, "%s: total rows %lld must be >= 0", who, (long long)rows);
     if (Hq <= 0 || Hkv <= 0) return fail(ATTN_E_INVALID_ARG, "%s: Hq=%d and Hkv=%d must be >= 1", who, Hq, Hkv);
     if (Hq % Hkv != 0) return fail(ATTN_E_INVALID_ARG, "%s: Hq=%d is not a multiple of Hkv=%d", who, Hq, Hkv);
     if (d_qk <= 0 || d_v <= 0) return fail(ATTN_E_INVALID_ARG, "%s: head dims d_qk=%d d_v=%d must be > 0", who, d_qk, d_v);
@@ -41,26 +46,69 @@ int check_common(const void* q, const void* k, const void* v, void* o, const flo
     if (d_qk != 128 && d_qk != 192) return fail(ATTN_E_UNSUPPORTED, "%s: d_qk=%d unsupported (128 or 192)", who, d_qk);
     if (d_v != 128) return fail(ATTN_E_UNSUPPORTED, "%s: d_v=%d unsupported (128)", who, d_v);
     // Every element offset is formed in 64-bit arithmetic by the kernels; the row
-    // index b*S+s and the head count must fit comfortably in 32-bit integers.
-    if ((int64_t)B * S > (int64_t)1 << 30) return fail(ATTN_E_UNSUPPORTED, "%s: B*S=%lld too large", who, (long long)B * S);
-    if (B == 0 || S == 0) return -1;
+    // index and the head count must fit comfortably in 32-bit integers.
+    if (rows > (int64_t)1 << 30 || (int64_t)B * S > (int64_t)1 << 30)
+        return fail(ATTN_E_UNSUPPORTED, "%s: %lld rows too many", who, (long long)std::max<int64_t>(rows, (int64_t)B * S));
+    if (B == 0 || S == 0 || rows == 0) return -1;
     if (!q || !k || !v || !o) return fail(ATTN_E_INVALID_ARG, "%s: null tensor pointer", who);
     if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o))
         return fail(ATTN_E_INVALID_ARG, "%s: tensor pointers must be 16-byte aligned", who);
-    const size_t nq = (size_t)B * S * Hq * d_qk * elem_qkv;
-    const size_t nk = (size_t)B * S * Hkv * d_qk * elem_qkv;
-    const size_t nv = (size_t)B * S * Hkv * d_v * elem_qkv;
-    const size_t no = (size_t)B * S * Hq * d_v * 2;
+    const size_t nq = (size_t)rows * Hq * d_qk * elem_qkv;
+    const size_t nk = (size_t)rows * Hkv * d_qk * elem_qkv;
+    const size_t nv = (size_t)rows * Hkv * d_v * elem_qkv;
+    const size_t no = (size_t)rows * Hq * d_v * 2;
     if (overlaps(o, no, q, nq) || overlaps(o, no, k, nk) || overlaps(o, no, v, nv))
         return fail(ATTN_E_INVALID_ARG, "%s: output overlaps an input", who);
     if (lse) {
         if ((reinterpret_cast<uintptr_t>(lse) & 3u) != 0)
             return fail(ATTN_E_INVALID_ARG, "%s: lse pointer must be 4-byte aligned", who);
-        const size_t nl = (size_t)B * Hq * S * sizeof(float);
+        const size_t nl = (size_t)rows * Hq * sizeof(float);
         if (overlaps(lse, nl, q, nq) || overlaps(lse, nl, k, nk) || overlaps(lse, nl, v, nv) || overlaps(lse, nl, o, no))
             return fail(ATTN_E_INVALID_ARG, "%s: lse overlaps another tensor", who);
     }
     return ATTN_OK;
+}
+
+// Checks of a variable-length batch's offsets pointer (its contents live on the
+// device and are clamped by the kernels, so any values stay in bounds).
+int check_cu(const int* cu, int n_seqs, const char* who) {
+    if (n_seqs > 0 && !cu) return fail(ATTN_E_INVALID_ARG, "%s: null cu_seqlens", who);
+    if (cu && (reinterpret_cast<uintptr_t>(cu) & 3u) != 0)
+        return fail(ATTN_E_INVALID_ARG, "%s: cu_seqlens must be 4-byte aligned", who);
+    return ATTN_OK;
+}
+
+int run_fp8(const void* q, const void* k, const void* v, void* o, float* lse, bool varlen, const int* cu, int total,
+            float q_scale, float k_scale, float v_scale, float softmax_scale, int B, int Hq, int Hkv, int S,
+            int d_qk, int d_v, int causal, int p_mode, hipStream_t stream, const char* who) {
+    const int64_t rows = varlen ? (int64_t)total : (int64_t)B * S;
+    int st = check_common(q, k, v, o, lse, softmax_scale, B, Hq, Hkv, S, rows, d_qk, d_v, causal, 1, who);
+    if (st == -1) { g_err[0] = 0; return ATTN_OK; }
+    if (st != ATTN_OK) return st;
+    if (!(std::isfinite(q_scale) && q_scale > 0.f) || !(std::isfinite(k_scale) && k_scale > 0.f) ||
+        !(std::isfinite(v_scale) && v_scale > 0.f))
+        return fail(ATTN_E_INVALID_ARG, "%s: q/k/v scales must be finite and > 0", who);
+    if (p_mode != ATTN_P_EXACT && p_mode != ATTN_P_LEAN)
+        return fail(ATTN_E_INVALID_ARG, "%s: p_mode=%d must be 0 (exact) or 1 (lean)", who, p_mode);
+    attnfwd::Problem p{q, k, v, o, q_scale, k_scale, v_scale,
+                       softmax_scale > 0.f ? softmax_scale : 1.0f / std::sqrt((float)d_qk),
+                       B, Hq, Hkv, S, d_qk, d_v, p_mode, stream, lse, causal, cu, (int)rows};
+    const double c = (double)q_scale * k_scale * p.sm * 1.4426950408889634;
+    if (!(c < 1e30 && c > 1e-30)) return fail(ATTN_E_INVALID_ARG, "%s: q_scale*k_scale*softmax_scale out of range", who);
+    return finish(attnfwd::launch_fp8(p), who);
+}
+
+int run_bf16(const void* q, const void* k, const void* v, void* o, float* lse, bool varlen, const int* cu, int total,
+             float softmax_scale, int B, int Hq, int Hkv, int S, int d_qk, int d_v, int causal,
+             hipStream_t stream, const char* who) {
+    const int64_t rows = varlen ? (int64_t)total : (int64_t)B * S;
+    int st = check_common(q, k, v, o, lse, softmax_scale, B, Hq, Hkv, S, rows, d_qk, d_v, causal, 2, who);
+    if (st == -1) { g_err[0] = 0; return ATTN_OK; }
+    if (st != ATTN_OK) return st;
+    attnfwd::Problem p{q, k, v, o, 1.f, 1.f, 1.f,
+                       softmax_scale > 0.f ? softmax_scale : 1.0f / std::sqrt((float)d_qk),
+                       B, Hq, Hkv, S, d_qk, d_v, 0, stream, lse, causal, cu, (int)rows};
+    return finish(attnfwd::launch_bf16(p), who);
 }
 
 int finish(hipError_t e, const char* who) {
@@ -77,21 +125,8 @@ int attn_fwd_fp8_lse(const void* q, const void* k, const void* v, void* o, float
                      float q_scale, float k_scale, float v_scale, float softmax_scale,
                      int B, int Hq, int Hkv, int S, int d_qk, int d_v,
                      int causal, int p_mode, hipStream_t stream) {
-    const char* who = lse ? "attn_fwd_fp8_lse" : "attn_fwd_fp8";
-    int st = check_common(q, k, v, o, lse, softmax_scale, B, Hq, Hkv, S, d_qk, d_v, causal, 1, who);
-    if (st == -1) { g_err[0] = 0; return ATTN_OK; }
-    if (st != ATTN_OK) return st;
-    if (!(std::isfinite(q_scale) && q_scale > 0.f) || !(std::isfinite(k_scale) && k_scale > 0.f) ||
-        !(std::isfinite(v_scale) && v_scale > 0.f))
-        return fail(ATTN_E_INVALID_ARG, "%s: q/k/v scales must be finite and > 0", who);
-    if (p_mode != ATTN_P_EXACT && p_mode != ATTN_P_LEAN)
-        return fail(ATTN_E_INVALID_ARG, "%s: p_mode=%d must be 0 (exact) or 1 (lean)", who, p_mode);
-    attnfwd::Problem p{q, k, v, o, q_scale, k_scale, v_scale,
-                       softmax_scale > 0.f ? softmax_scale : 1.0f / std::sqrt((float)d_qk),
-                       B, Hq, Hkv, S, d_qk, d_v, p_mode, stream, lse, causal};
-    const double c = (double)q_scale * k_scale * p.sm * 1.4426950408889634;
-    if (!(c < 1e30 && c > 1e-30)) return fail(ATTN_E_INVALID_ARG, "%s: q_scale*k_scale*softmax_scale out of range", who);
-    return finish(attnfwd::launch_fp8(p), who);
+    return run_fp8(q, k, v, o, lse, false, nullptr, 0, q_scale, k_scale, v_scale, softmax_scale, B, Hq, Hkv, S, d_qk, d_v,
+                   causal, p_mode, stream, lse ? "attn_fwd_fp8_lse" : "attn_fwd_fp8");
 }
 
 int attn_fwd_fp8(const void* q, const void* k, const void* v, void* o,
@@ -102,21 +137,34 @@ int attn_fwd_fp8(const void* q, const void* k, const void* v, void* o,
                             B, Hq, Hkv, S, d_qk, d_v, causal, p_mode, stream);
 }
 
+int attn_fwd_fp8_varlen(const void* q, const void* k, const void* v, void* o, float* lse,
+                        const int* cu_seqlens, int n_seqs, int max_seqlen, int total_tokens,
+                        float q_scale, float k_scale, float v_scale, float softmax_scale,
+                        int Hq, int Hkv, int d_qk, int d_v, int causal, int p_mode, hipStream_t stream) {
+    const char* who = "attn_fwd_fp8_varlen";
+    if (int st = check_cu(cu_seqlens, n_seqs, who)) return st;
+    return run_fp8(q, k, v, o, lse, true, cu_seqlens, total_tokens, q_scale, k_scale,
+                   v_scale, softmax_scale, n_seqs, Hq, Hkv, max_seqlen, d_qk, d_v, causal, p_mode, stream, who);
+}
+
 int attn_fwd_bf16_lse(const void* q, const void* k, const void* v, void* o, float* lse, float softmax_scale,
                       int B, int Hq, int Hkv, int S, int d_qk, int d_v, int causal, hipStream_t stream) {
-    const char* who = lse ? "attn_fwd_bf16_lse" : "attn_fwd_bf16";
-    int st = check_common(q, k, v, o, lse, softmax_scale, B, Hq, Hkv, S, d_qk, d_v, causal, 2, who);
-    if (st == -1) { g_err[0] = 0; return ATTN_OK; }
-    if (st != ATTN_OK) return st;
-    attnfwd::Problem p{q, k, v, o, 1.f, 1.f, 1.f,
-                       softmax_scale > 0.f ? softmax_scale : 1.0f / std::sqrt((float)d_qk),
-                       B, Hq, Hkv, S, d_qk, d_v, 0, stream, lse, causal};
-    return finish(attnfwd::launch_bf16(p), who);
+    return run_bf16(q, k, v, o, lse, false, nullptr, 0, softmax_scale, B, Hq, Hkv, S, d_qk, d_v, causal, stream,
+                    lse ? "attn_fwd_bf16_lse" : "attn_fwd_bf16");
 }
 
 int attn_fwd_bf16(const void* q, const void* k, const void* v, void* o, float softmax_scale,
                   int B, int Hq, int Hkv, int S, int d_qk, int d_v, int causal, hipStream_t stream) {
     return attn_fwd_bf16_lse(q, k, v, o, nullptr, softmax_scale, B, Hq, Hkv, S, d_qk, d_v, causal, stream);
+}
+
+int attn_fwd_bf16_varlen(const void* q, const void* k, const void* v, void* o, float* lse,
+                         const int* cu_seqlens, int n_seqs, int max_seqlen, int total_tokens,
+                         float softmax_scale, int Hq, int Hkv, int d_qk, int d_v, int causal, hipStream_t stream) {
+    const char* who = "attn_fwd_bf16_varlen";
+    if (int st = check_cu(cu_seqlens, n_seqs, who)) return st;
+    return run_bf16(q, k, v, o, lse, true, cu_seqlens, total_tokens, softmax_scale, n_seqs,
+                    Hq, Hkv, max_seqlen, d_qk, d_v, causal, stream, who);
 }
 
 int attn_rotate_quant_bf16(const void* x, void* x8, float* scale, int B, int S, int H, int d,
@@ -139,6 +187,6 @@ int attn_rotate_quant_bf16(const void* x, void* x8, float* scale, int B, int S, 
 
 const char* attn_last_error(void) { return g_err; }
 
-int attn_abi_version(void) { return 101; }
+int attn_abi_version(void) { return 102; }
 
 }  // extern "C"

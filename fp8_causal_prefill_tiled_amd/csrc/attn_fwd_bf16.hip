@@ -66,6 +66,8 @@ struct Bf16Params {
     float c;      // sm * log2(e)
     int B, Hq, Hkv, S;
     int n_tiles;
+    const int* cu;  // variable-length batches: B + 1 token offsets (device), else null
+    int total;      // variable-length batches: rows of the packed tensors
 };
 
 // 16-byte chunk swizzle of a V row (16 chunks of 8 bf16).  A transposing read of
@@ -80,7 +82,7 @@ __device__ __forceinline__ void mfma_bf16_vacc(f32x16& acc, const bf16x8& a, con
     asm("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(acc) : "v"(a), "v"(b));
 }
 
-template <int DQK, bool CAUSAL, bool LSE>
+template <int DQK, bool CAUSAL, bool LSE, bool VARLEN>
 __global__ void __launch_bounds__(512) bf16_causal_fwd(Bf16Params a) {
     using T = Bf16Tile<DQK>;
     constexpr int NT = 256;                       // threads per group
@@ -105,7 +107,19 @@ __global__ void __launch_bounds__(512) bf16_causal_fwd(Bf16Params a) {
     const int b = bh / a.Hq;
     const int h = bh - b * a.Hq;
     const int g = h / (a.Hq / a.Hkv);
-    const int S = a.S;
+    // Sequence b: S rows starting at packed row tok0.  Equal-length batches are
+    // (B, S, H, d); a variable-length batch packs its sequences along the rows and
+    // a.S is the longest one.  The offsets are clamped into [0, total], so any
+    // contents of cu keep every access inside the tensors.
+    int S = a.S;
+    int64_t tok0 = (int64_t)b * S;
+    if constexpr (VARLEN) {
+        const int t0 = min(max(a.cu[b], 0), a.total);
+        const int t1 = min(max(a.cu[b + 1], t0), a.total);
+        S = min(t1 - t0, a.S);
+        tok0 = t0;
+        if (tile * BM >= S) return;   // whole workgroup: past the end of this sequence
+    }
     const int q0 = tile * BM;
     const int kend = CAUSAL ? min(S, q0 + BM) : S;
     const int nblk = (kend + KB - 1) / KB;        // key blocks the workgroup walks
@@ -119,15 +133,15 @@ __global__ void __launch_bounds__(512) bf16_causal_fwd(Bf16Params a) {
     const int64_t q_row = (int64_t)a.Hq * DQK;    // elements between consecutive queries
     const int k_row = a.Hkv * DQK * 2;            // bytes between consecutive keys
     const int v_row = a.Hkv * 128 * 2;
-    const uint8_t* kbase = reinterpret_cast<const uint8_t*>(a.k) + ((int64_t)b * S * a.Hkv + g) * DQK * 2;
-    const uint8_t* vbase = reinterpret_cast<const uint8_t*>(a.v) + ((int64_t)b * S * a.Hkv + g) * 128 * 2;
+    const uint8_t* kbase = reinterpret_cast<const uint8_t*>(a.k) + (tok0 * a.Hkv + g) * DQK * 2;
+    const uint8_t* vbase = reinterpret_cast<const uint8_t*>(a.v) + (tok0 * a.Hkv + g) * 128 * 2;
 
     // Q^T operand: lane (query c, half hh) holds d in [16ks + 8hh, +8) for each step ks.
     bf16x8 qreg[T::NKS];
     {
         const bool ok = qabs < S;
         const uint8_t* qp = reinterpret_cast<const uint8_t*>(
-            a.q + ((int64_t)b * S + (ok ? qabs : 0)) * q_row + (int64_t)h * DQK + 8 * hh);
+            a.q + (tok0 + (ok ? qabs : 0)) * q_row + (int64_t)h * DQK + 8 * hh);
 #pragma unroll
         for (int ks = 0; ks < T::NKS; ++ks) {
             i32x4 x = ok ? load16(qp + 32 * ks) : i32x4{0, 0, 0, 0};
@@ -412,9 +426,9 @@ __global__ void __launch_bounds__(512) bf16_causal_fwd(Bf16Params a) {
     // l = sum_j 2^(t_j - ref), so the row's natural-log normaliser is ln2 * (log2 l + ref).
     const float lsum = lpart + other_half(lpart);
     if (LSE && hh == 0 && qabs < S)
-        a.lse[((int64_t)b * a.Hq + h) * S + qabs] = (log2f(lsum) + ref) * 0.6931471805599453f;
+        a.lse[(VARLEN ? (int64_t)h * a.total + tok0 : ((int64_t)b * a.Hq + h) * S) + qabs] = (log2f(lsum) + ref) * 0.6931471805599453f;
     if (qabs < S) {
-        __bf16* op = a.o + (((int64_t)b * S + qabs) * a.Hq + h) * 128;
+        __bf16* op = a.o + ((tok0 + qabs) * a.Hq + h) * 128;
 #pragma unroll
         for (int dt = 0; dt < 4; ++dt) {
 #pragma unroll
@@ -430,7 +444,7 @@ __global__ void __launch_bounds__(512) bf16_causal_fwd(Bf16Params a) {
     }
 }
 
-template <int DQK, bool CAUSAL, bool LSE>
+template <int DQK, bool CAUSAL, bool LSE, bool VARLEN>
 hipError_t launch_t(const Problem& p) {
     constexpr int BM = 256;
     Bf16Params a;
@@ -444,27 +458,32 @@ hipError_t launch_t(const Problem& p) {
     a.Hq = p.Hq;
     a.Hkv = p.Hkv;
     a.S = p.S;
+    a.cu = p.cu;
+    a.total = p.total;
     a.n_tiles = (p.S + BM - 1) / BM;
     const long long nblocks = (long long)a.n_tiles * p.B * p.Hq;
     if (nblocks <= 0 || nblocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-    hipLaunchKernelGGL((bf16_causal_fwd<DQK, CAUSAL, LSE>), dim3((unsigned)nblocks), dim3(512), 0, p.stream, a);
+    hipLaunchKernelGGL((bf16_causal_fwd<DQK, CAUSAL, LSE, VARLEN>), dim3((unsigned)nblocks), dim3(512), 0, p.stream, a);
     return hipGetLastError();
 }
 
 // The log-sum-exp store is a template switch: the kernels without it keep exactly the
 // code they have when no caller asks for it.
-template <bool CAUSAL, bool LSE>
+template <bool CAUSAL, bool LSE, bool VARLEN>
 hipError_t launch_c(const Problem& p) {
-    if (p.d_qk == 128) return launch_t<128, CAUSAL, LSE>(p);
-    if (p.d_qk == 192) return launch_t<192, CAUSAL, LSE>(p);
+    if (p.d_qk == 128) return launch_t<128, CAUSAL, LSE, VARLEN>(p);
+    if (p.d_qk == 192) return launch_t<192, CAUSAL, LSE, VARLEN>(p);
     return hipErrorInvalidValue;
+}
+
+template <bool VARLEN>
+hipError_t launch_v(const Problem& p) {
+    if (p.lse) return p.causal ? launch_c<true, true, VARLEN>(p) : launch_c<false, true, VARLEN>(p);
+    return p.causal ? launch_c<true, false, VARLEN>(p) : launch_c<false, false, VARLEN>(p);
 }
 
 }  // namespace
 
-hipError_t launch_bf16(const Problem& p) {
-    if (p.lse) return p.causal ? launch_c<true, true>(p) : launch_c<false, true>(p);
-    return p.causal ? launch_c<true, false>(p) : launch_c<false, false>(p);
-}
+hipError_t launch_bf16(const Problem& p) { return p.cu ? launch_v<true>(p) : launch_v<false>(p); }
 
 }  // namespace attnfwd

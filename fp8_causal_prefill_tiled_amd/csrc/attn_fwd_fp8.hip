@@ -60,6 +60,8 @@ struct Fp8Params {
     float v_scale;
     int B, Hq, Hkv, S;
     int n_tiles;    // query tiles per head
+    const int* cu;  // variable-length batches: B + 1 token offsets (device), else null
+    int total;      // variable-length batches: rows of the packed tensors
 };
 
 // 16-byte chunk swizzle of a V row in LDS.  The transposing read of one 16-lane
@@ -96,7 +98,7 @@ __device__ __forceinline__ int v_swz(int row) { return (row & 3) | (((row >> 3) 
 // workgroup with the transposing ds_read_b64_tr_b8, far slower per byte than
 // ds_read_b128 on gfx950.  Buffer loads use a range ending at row S, so rows
 // past S read as zeros.
-template <int DQK, int PMODE, bool CAUSAL, bool LSE>
+template <int DQK, int PMODE, bool CAUSAL, bool LSE, bool VARLEN>
 __global__ void __launch_bounds__(512) fp8_causal_fwd(Fp8Params a) {
     using T = Fp8Tile<DQK>;
     constexpr int NT = 256;                       // threads per group
@@ -123,7 +125,19 @@ __global__ void __launch_bounds__(512) fp8_causal_fwd(Fp8Params a) {
     const int b = bh / a.Hq;
     const int h = bh - b * a.Hq;
     const int g = h / (a.Hq / a.Hkv);
-    const int S = a.S;
+    // Sequence b: S rows starting at packed row tok0.  Equal-length batches are
+    // (B, S, H, d); a variable-length batch packs its sequences along the rows and
+    // a.S is the longest one.  The offsets are clamped into [0, total], so any
+    // contents of cu keep every access inside the tensors.
+    int S = a.S;
+    int64_t tok0 = (int64_t)b * S;
+    if constexpr (VARLEN) {
+        const int t0 = min(max(a.cu[b], 0), a.total);
+        const int t1 = min(max(a.cu[b + 1], t0), a.total);
+        S = min(t1 - t0, a.S);
+        tok0 = t0;
+        if (tile * BM >= S) return;   // whole workgroup: past the end of this sequence
+    }
     const int q0 = tile * BM;
     const int kend = CAUSAL ? min(S, q0 + BM) : S;
     const int nblk = (kend + KB - 1) / KB;        // key blocks the workgroup walks
@@ -137,14 +151,14 @@ __global__ void __launch_bounds__(512) fp8_causal_fwd(Fp8Params a) {
     const int64_t q_row = (int64_t)a.Hq * DQK;
     const int k_row = a.Hkv * DQK;                // bytes between consecutive keys
     const int v_row = a.Hkv * 128;
-    const uint8_t* kbase = a.k + (int64_t)b * S * k_row + (int64_t)g * DQK;
-    const uint8_t* vbase = a.v + (int64_t)b * S * v_row + (int64_t)g * 128;
+    const uint8_t* kbase = a.k + tok0 * k_row + (int64_t)g * DQK;
+    const uint8_t* vbase = a.v + tok0 * v_row + (int64_t)g * 128;
 
     // Q^T operands: lane (query c, half hh) holds d in [64kk + 32hh, +32) for each step kk.
     i32x8 qr[T::NKK];
     {
         const bool ok = qabs < S;
-        const uint8_t* qp = a.q + ((int64_t)b * S + (ok ? qabs : 0)) * q_row + (int64_t)h * DQK + 32 * hh;
+        const uint8_t* qp = a.q + (tok0 + (ok ? qabs : 0)) * q_row + (int64_t)h * DQK + 32 * hh;
 #pragma unroll
         for (int kk = 0; kk < T::NKK; ++kk) {
             i32x4 lo = ok ? load16(qp + 64 * kk) : i32x4{0, 0, 0, 0};
@@ -463,9 +477,9 @@ __global__ void __launch_bounds__(512) fp8_causal_fwd(Fp8Params a) {
     // probabilities, so the row's natural-log normaliser is ln2 * (log2 L + ref).
     const float l0 = lsum[0];
     if (LSE && hh == 0 && qabs < S)
-        a.lse[((int64_t)b * a.Hq + h) * S + qabs] = (log2f(l0) + ref) * 0.6931471805599453f;
+        a.lse[(VARLEN ? (int64_t)h * a.total + tok0 : ((int64_t)b * a.Hq + h) * S) + qabs] = (log2f(l0) + ref) * 0.6931471805599453f;
     if (qabs < S) {
-        __bf16* op = a.o + (((int64_t)b * S + qabs) * a.Hq + h) * 128;
+        __bf16* op = a.o + ((tok0 + qabs) * a.Hq + h) * 128;
 #pragma unroll
         for (int dt = 0; dt < 4; ++dt) {
 #pragma unroll
@@ -481,7 +495,7 @@ __global__ void __launch_bounds__(512) fp8_causal_fwd(Fp8Params a) {
     }
 }
 
-template <int DQK, int PMODE, bool CAUSAL, bool LSE>
+template <int DQK, int PMODE, bool CAUSAL, bool LSE, bool VARLEN>
 hipError_t launch_t(const Problem& p) {
     constexpr int NW = 8;
     constexpr int BM = 256;
@@ -499,27 +513,34 @@ hipError_t launch_t(const Problem& p) {
     a.Hq = p.Hq;
     a.Hkv = p.Hkv;
     a.S = p.S;
+    a.cu = p.cu;
+    a.total = p.total;
     a.n_tiles = (p.S + BM - 1) / BM;
     const long long nblocks = (long long)a.n_tiles * p.B * p.Hq;
     if (nblocks <= 0 || nblocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-    hipLaunchKernelGGL((fp8_causal_fwd<DQK, PMODE, CAUSAL, LSE>), dim3((unsigned)nblocks), dim3(NW * 64), 0, p.stream, a);
+    hipLaunchKernelGGL((fp8_causal_fwd<DQK, PMODE, CAUSAL, LSE, VARLEN>), dim3((unsigned)nblocks), dim3(NW * 64), 0, p.stream, a);
     return hipGetLastError();
 }
 
 // The log-sum-exp store is a template switch: the kernels without it keep exactly the
 // code (and code layout) they have when no caller asks for it.
-template <bool CAUSAL, bool LSE>
+template <bool CAUSAL, bool LSE, bool VARLEN>
 hipError_t launch_c(const Problem& p) {
-    if (p.d_qk == 128) return p.p_mode == 0 ? launch_t<128, 0, CAUSAL, LSE>(p) : launch_t<128, 1, CAUSAL, LSE>(p);
-    if (p.d_qk == 192) return p.p_mode == 0 ? launch_t<192, 0, CAUSAL, LSE>(p) : launch_t<192, 1, CAUSAL, LSE>(p);
+    if (p.d_qk == 128)
+        return p.p_mode == 0 ? launch_t<128, 0, CAUSAL, LSE, VARLEN>(p) : launch_t<128, 1, CAUSAL, LSE, VARLEN>(p);
+    if (p.d_qk == 192)
+        return p.p_mode == 0 ? launch_t<192, 0, CAUSAL, LSE, VARLEN>(p) : launch_t<192, 1, CAUSAL, LSE, VARLEN>(p);
     return hipErrorInvalidValue;
+}
+
+template <bool VARLEN>
+hipError_t launch_v(const Problem& p) {
+    if (p.lse) return p.causal ? launch_c<true, true, VARLEN>(p) : launch_c<false, true, VARLEN>(p);
+    return p.causal ? launch_c<true, false, VARLEN>(p) : launch_c<false, false, VARLEN>(p);
 }
 
 }  // namespace
 
-hipError_t launch_fp8(const Problem& p) {
-    if (p.lse) return p.causal ? launch_c<true, true>(p) : launch_c<false, true>(p);
-    return p.causal ? launch_c<true, false>(p) : launch_c<false, false>(p);
-}
+hipError_t launch_fp8(const Problem& p) { return p.cu ? launch_v<true>(p) : launch_v<false>(p); }
 
 }  // namespace attnfwd

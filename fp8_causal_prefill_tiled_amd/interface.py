@@ -1,0 +1,114 @@
+"""``flash_attn_func``-style entry point and torch.library custom operators.
+
+The pages describe the kernels as a drop-in replacement for ``flash_attn_func``
+("Zyphra ZYFA: FP8 FlashAttention for AMD MI355X, Up to 1.76x Faster", TL;DR).
+This module gives that calling convention over the C ABI, and registers the two
+attention calls as torch custom operators (``fp8_prefill::attn_fwd_fp8`` and
+``fp8_prefill::attn_fwd_bf16``) with shape-only fake implementations, so that
+``torch.compile`` traces them as single opaque nodes instead of breaking the graph.
+
+Every call still runs in the library's HIP kernels through ``binding``; this
+module holds no attention arithmetic and no fallback.
+"""
+import torch
+
+from . import binding
+
+_OPS = "fp8_prefill"
+_FP8_DTYPES = (torch.float8_e4m3fn, torch.uint8)
+
+
+@torch.library.custom_op(f"{_OPS}::attn_fwd_fp8", mutates_args=(), device_types="cuda")
+def _attn_fwd_fp8_op(q8: torch.Tensor, k8: torch.Tensor, v8: torch.Tensor, q_scale: float, k_scale: float,
+                     v_scale: float, softmax_scale: float, causal: bool, p_mode: int, with_lse: bool
+                     ) -> tuple[torch.Tensor, torch.Tensor]:
+    sm = softmax_scale if softmax_scale > 0 else None
+    if not with_lse:
+        out = binding.attn_fwd_fp8(q8, k8, v8, q_scale, k_scale, v_scale, softmax_scale=sm, causal=causal,
+                                   p_mode=p_mode)
+        return out, q8.new_empty((0,), dtype=torch.float32)
+    return binding.attn_fwd_fp8(q8, k8, v8, q_scale, k_scale, v_scale, softmax_scale=sm, causal=causal,
+                                p_mode=p_mode, return_lse=True)
+
+
+def _fake_outputs(q, v, with_lse):
+    B, S, Hq, _ = q.shape
+    lse_shape = (B, Hq, S) if with_lse else (0,)
+    return (q.new_empty((B, S, Hq, v.shape[3]), dtype=torch.bfloat16),
+            q.new_empty(lse_shape, dtype=torch.float32))
+
+
+@_attn_fwd_fp8_op.register_fake
+def _(q8, k8, v8, q_scale, k_scale, v_scale, softmax_scale, causal, p_mode, with_lse):
+    return _fake_outputs(q8, v8, with_lse)
+
+
+@torch.library.custom_op(f"{_OPS}::attn_fwd_bf16", mutates_args=(), device_types="cuda")
+def _attn_fwd_bf16_op(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, softmax_scale: float, causal: bool,
+                      with_lse: bool) -> tuple[torch.Tensor, torch.Tensor]:
+    sm = softmax_scale if softmax_scale > 0 else None
+    if not with_lse:
+        return binding.attn_fwd_bf16(q, k, v, softmax_scale=sm, causal=causal), q.new_empty((0,), dtype=torch.float32)
+    return binding.attn_fwd_bf16(q, k, v, softmax_scale=sm, causal=causal, return_lse=True)
+
+
+@_attn_fwd_bf16_op.register_fake
+def _(q, k, v, softmax_scale, causal, with_lse):
+    return _fake_outputs(q, v, with_lse)
+
+
+def _scale(x, name):
+    if x is None:
+        raise ValueError(f"FP8 inputs need {name} (the per-tensor dequantisation scale)")
+    if isinstance(x, torch.Tensor):
+        if x.numel() != 1:
+            raise ValueError(f"{name} must be a single per-tensor scale, got {x.numel()} elements")
+        x = float(x.item())
+    return float(x)
+
+
+def flash_attn_func(q, k, v, dropout_p=0.0, softmax_scale=None, causal=False, window_size=(-1, -1),
+                    softcap=0.0, alibi_slopes=None, deterministic=False, return_attn_probs=False, *,
+                    q_descale=None, k_descale=None, v_descale=None, p_mode="lean"):
+    """Forward attention in the ``flash_attn_func`` calling convention.
+
+    q: (B, S, Hq, d_qk), k: (B, S, Hkv, d_qk), v: (B, S, Hkv, d_v), contiguous, on
+    the GPU, equal query and key lengths.  bfloat16 inputs run the BF16 kernel;
+    float8_e4m3fn (or uint8 e4m3 bytes) inputs run the FP8 kernel and need the
+    per-tensor scales ``q_descale``/``k_descale``/``v_descale`` (float or
+    one-element tensor: dequantised value = descale * code), with ``p_mode``
+    "lean" or "exact".  Returns the bf16 output (B, S, Hq, d_v); with
+    ``return_attn_probs`` returns (out, lse, None), lse fp32 (B, Hq, S), as
+    flash_attn_func does (its third value, the dropout mask, is always None).
+    Scales given as tensors are read with ``.item()`` (a host sync); pass
+    floats inside ``torch.compile``d code.
+
+    Options outside the kernels' scope raise NotImplementedError: dropout,
+    sliding windows, softcapping and ALiBi.  ``deterministic`` is accepted and
+    always holds (fixed reduction order, no atomics).
+    """
+    if dropout_p != 0.0:
+        raise NotImplementedError("dropout is not supported (forward inference kernels)")
+    if tuple(window_size) != (-1, -1):
+        raise NotImplementedError("sliding-window attention is not supported")
+    if softcap != 0.0:
+        raise NotImplementedError("softcapping is not supported")
+    if alibi_slopes is not None:
+        raise NotImplementedError("ALiBi is not supported")
+    sm = 0.0 if softmax_scale is None else float(softmax_scale)
+    if q.dtype in _FP8_DTYPES:
+        if k.dtype not in _FP8_DTYPES or v.dtype not in _FP8_DTYPES:
+            raise TypeError("q, k and v must all be FP8 e4m3 (or all bfloat16)")
+        q8, k8, v8 = (t.view(torch.uint8) if t.dtype != torch.uint8 else t for t in (q, k, v))
+        out, lse = _attn_fwd_fp8_op(q8, k8, v8, _scale(q_descale, "q_descale"), _scale(k_descale, "k_descale"),
+                                    _scale(v_descale, "v_descale"), sm, bool(causal),
+                                    int(binding._P_MODES[p_mode]), bool(return_attn_probs))
+    elif q.dtype == torch.bfloat16:
+        if k.dtype != torch.bfloat16 or v.dtype != torch.bfloat16:
+            raise TypeError("q, k and v must all be bfloat16 (or all FP8 e4m3)")
+        out, lse = _attn_fwd_bf16_op(q, k, v, sm, bool(causal), bool(return_attn_probs))
+    else:
+        raise TypeError(f"unsupported input dtype {q.dtype}: bfloat16 or float8_e4m3fn")
+    if return_attn_probs:
+        return out, lse, None
+    return out

@@ -165,6 +165,39 @@ int attn_fwd_bf16_lse(const void* q, const void* k, const void* v, void* o, floa
 int attn_rotate_quant_bf16(const void* x, void* x8, float* scale, int B, int S, int H, int d,
                            hipStream_t stream);
 
+/*
+ * Variable-length batches: n_seqs sequences of different lengths packed along
+ * the rows (the flash_attn_varlen_func convention), each attending only to
+ * itself (causal within the sequence when causal == 1).  The pages list
+ * variable batch sizing among what their kernels do not yet cover ("Breaking
+ * the FP8 Attention Bottleneck on AMD MI355X", section "Application Boundaries
+ * and Engineering Decisions"); this is the same kernel with per-sequence row
+ * offsets.
+ *
+ * q: (total_tokens, Hq, d_qk), k: (total_tokens, Hkv, d_qk), v: (total_tokens,
+ *    Hkv, d_v), o: (total_tokens, Hq, d_v) bf16, contiguous, 16-byte aligned.
+ * cu_seqlens: device pointer to n_seqs + 1 int32 row offsets, 4-byte aligned:
+ *    sequence i is rows cu_seqlens[i] .. cu_seqlens[i+1]-1.  Expected:
+ *    cu_seqlens[0] = 0, non-decreasing, cu_seqlens[n_seqs] <= total_tokens,
+ *    every length <= max_seqlen.  The contents are not read on the host (no
+ *    synchronisation); the kernels clamp every offset into [0, total_tokens] and
+ *    every length to max_seqlen, so any contents keep all accesses in bounds.
+ *    Rows outside every sequence are left unwritten.
+ * lse: NULL, or Hq * total_tokens floats, layout (Hq, total_tokens).
+ * The grid covers ceil(max_seqlen / 256) query tiles per (sequence, head);
+ * tiles past a sequence's end exit at once.  Other arguments, behaviour and
+ * errors as attn_fwd_fp8_lse / attn_fwd_bf16_lse; n_seqs == 0, max_seqlen == 0
+ * or total_tokens == 0 is an empty problem (ATTN_OK, nothing launched).
+ */
+int attn_fwd_fp8_varlen(const void* q, const void* k, const void* v, void* o, float* lse,
+                        const int* cu_seqlens, int n_seqs, int max_seqlen, int total_tokens,
+                        float q_scale, float k_scale, float v_scale, float softmax_scale,
+                        int Hq, int Hkv, int d_qk, int d_v, int causal, int p_mode, hipStream_t stream);
+int attn_fwd_bf16_varlen(const void* q, const void* k, const void* v, void* o, float* lse,
+                         const int* cu_seqlens, int n_seqs, int max_seqlen, int total_tokens,
+                         float softmax_scale, int Hq, int Hkv, int d_qk, int d_v, int causal,
+                         hipStream_t stream);
+
 /* Message for the calling thread's last non-OK status ("" if none).  The
  * returned storage is thread-local and valid until that thread's next call. */
 const char* attn_last_error(void);

@@ -33,10 +33,10 @@ def declared_functions():
 
 def test_exports_every_declared_symbol(lib):
     decl = declared_functions()
-    assert {"attn_fwd_fp8", "attn_fwd_fp8_lse", "attn_fwd_bf16", "attn_fwd_bf16_lse", "attn_last_error",
-            "attn_abi_version"} <= decl
+    assert {"attn_fwd_fp8", "attn_fwd_fp8_lse", "attn_fwd_fp8_varlen", "attn_fwd_bf16", "attn_fwd_bf16_lse",
+            "attn_fwd_bf16_varlen", "attn_last_error", "attn_abi_version"} <= decl
     assert decl <= binding.exported_symbols()
-    assert lib.attn_abi_version() == 101
+    assert lib.attn_abi_version() == 102
 
 
 # fake, never-dereferenced, 16-byte aligned device addresses of disjoint buffers
@@ -125,6 +125,36 @@ def test_lse_host_validation(lib, entry, kw, status):
     assert (msg == "") == (status == OK)
     if status != OK:
         assert msg.startswith(f"attn_fwd_{entry}_lse")
+
+
+CU = 0x60000000
+
+
+@pytest.mark.parametrize("entry", ["fp8", "bf16"])
+@pytest.mark.parametrize("kw,status", [
+    (dict(cu_seqlens=0), INVALID),                          # null offsets with sequences
+    (dict(cu_seqlens=CU + 2), INVALID),                     # misaligned offsets
+    (dict(total_tokens=-1), INVALID), (dict(max_seqlen=-1), INVALID), (dict(n_seqs=-1), INVALID),
+    (dict(total_tokens=(1 << 30) + 1), UNSUPPORTED),
+    (dict(d_qk=64), UNSUPPORTED), (dict(Hq=3), INVALID), (dict(causal=2), INVALID),
+    (dict(lse=Q + 64), INVALID),                            # lse inside Q
+    (dict(o=Q + 4096), INVALID),                            # output overlaps Q
+    (dict(n_seqs=0, cu_seqlens=0, q=0, k=0, v=0, o=0), OK),  # empty: nothing launched
+    (dict(total_tokens=0, q=0, k=0, v=0, o=0), OK),
+    (dict(max_seqlen=0, q=0, k=0, v=0, o=0), OK),
+])
+def test_varlen_host_validation(lib, entry, kw, status):
+    a = dict(q=Q, k=K, v=V, o=O, lse=LSE, cu_seqlens=CU, n_seqs=3, max_seqlen=100, total_tokens=200,
+             softmax_scale=0.0, Hq=4, Hkv=2, d_qk=128, d_v=128, causal=1)
+    if entry == "fp8":
+        a.update(q_scale=1.0, k_scale=1.0, v_scale=1.0, p_mode=1)
+    a.update(kw)
+    st = (binding.attn_fwd_fp8_varlen_raw if entry == "fp8" else binding.attn_fwd_bf16_varlen_raw)(**a)
+    assert st == status
+    msg = binding.attn_last_error()
+    assert (msg == "") == (status == OK)
+    if status != OK:
+        assert msg.startswith(f"attn_fwd_{entry}_varlen")
 
 
 def rotq(**kw):

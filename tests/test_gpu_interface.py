@@ -1,0 +1,73 @@
+"""GPU checks of the flash_attn_func-style wrapper and the torch custom operators: the
+same bytes as the direct binding calls (every call runs the HIP kernels), the same
+bytes under torch.compile (the operators trace as opaque nodes, no graph break), and
+torch.library.opcheck's registration checks."""
+import pytest
+import torch
+
+from fp8_causal_prefill_tiled_amd import binding
+from fp8_causal_prefill_tiled_amd import workloads as W
+from fp8_causal_prefill_tiled_amd.interface import flash_attn_func, _attn_fwd_bf16_op, _attn_fwd_fp8_op
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+
+
+def _fp8(S=300, Hq=4, Hkv=2, dqk=128, seed=8):
+    d = W.make_fp8(W.Workload("iface", 1, Hq, Hkv, S, dqk, 128), seed=seed)
+    q8, k8, v8 = (d[n].to(DEV) for n in ("q8", "k8", "v8"))
+    return d, q8, k8, v8
+
+
+@pytest.mark.parametrize("causal", [True, False])
+@pytest.mark.parametrize("mode", ["lean", "exact"])
+def test_fp8_wrapper_matches_binding(mode, causal):
+    d, q8, k8, v8 = _fp8()
+    ref, ref_lse = binding.attn_fwd_fp8(q8, k8, v8, d["q_scale"], d["k_scale"], d["v_scale"], p_mode=mode,
+                                        causal=causal, return_lse=True)
+    qf, kf, vf = (t.view(torch.float8_e4m3fn) for t in (q8, k8, v8))
+    scales = dict(q_descale=d["q_scale"], k_descale=torch.tensor([d["k_scale"]], device=DEV),
+                  v_descale=d["v_scale"])
+    out, lse, none = flash_attn_func(qf, kf, vf, causal=causal, return_attn_probs=True, p_mode=mode, **scales)
+    out2 = flash_attn_func(qf, kf, vf, causal=causal, p_mode=mode, **scales)
+    torch.cuda.synchronize()
+    assert none is None
+    assert torch.equal(out.view(torch.int16), ref.view(torch.int16))
+    assert torch.equal(out2.view(torch.int16), ref.view(torch.int16))
+    assert torch.equal(lse, ref_lse)
+
+
+@pytest.mark.parametrize("causal", [True, False])
+def test_bf16_wrapper_matches_binding(causal):
+    d = W.make_bf16(W.Workload("iface", 2, 4, 2, 257, 192, 128), seed=9)
+    q, k, v = (d[n].to(DEV) for n in ("q", "k", "v"))
+    ref, ref_lse = binding.attn_fwd_bf16(q, k, v, causal=causal, return_lse=True, softmax_scale=0.07)
+    out, lse, _ = flash_attn_func(q, k, v, causal=causal, softmax_scale=0.07, return_attn_probs=True)
+    torch.cuda.synchronize()
+    assert torch.equal(out.view(torch.int16), ref.view(torch.int16)) and torch.equal(lse, ref_lse)
+
+
+def test_torch_compile_full_graph_same_bytes():
+    d, q8, k8, v8 = _fp8(S=200)
+    qb, kb, vb = (W.make_bf16(W.Workload("iface", 1, 4, 2, 200, 128, 128), seed=3)[n].to(DEV) for n in "qkv")
+    qs, ks, vs = d["q_scale"], d["k_scale"], d["v_scale"]
+
+    def f(q8, k8, v8, qb, kb, vb):
+        a = flash_attn_func(q8, k8, v8, causal=True, q_descale=qs, k_descale=ks, v_descale=vs)
+        b, lse, _ = flash_attn_func(qb, kb, vb, causal=True, return_attn_probs=True)
+        return a.float() + b.float(), lse
+
+    qf, kf, vf = (t.view(torch.float8_e4m3fn) for t in (q8, k8, v8))
+    eager = f(qf, kf, vf, qb, kb, vb)
+    compiled = torch.compile(f, backend="aot_eager", fullgraph=True)(qf, kf, vf, qb, kb, vb)
+    torch.cuda.synchronize()
+    assert torch.equal(eager[0], compiled[0]) and torch.equal(eager[1], compiled[1])
+
+
+def test_opcheck():
+    d, q8, k8, v8 = _fp8(S=130)
+    torch.library.opcheck(_attn_fwd_fp8_op, (q8, k8, v8, d["q_scale"], d["k_scale"], d["v_scale"], 0.0, True, 1,
+                                             True))
+    b = W.make_bf16(W.Workload("iface", 1, 4, 2, 130, 128, 128), seed=4)
+    q, k, v = (b[n].to(DEV) for n in ("q", "k", "v"))
+    torch.library.opcheck(_attn_fwd_bf16_op, (q, k, v, 0.0, False, True))
