@@ -39,10 +39,25 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-rotate", action="store_true",
                     help="skip timing the Hadamard rotation + quantisation of Q and K")
+    ap.add_argument("--input-study", action="store_true",
+                    help="also time the FP8 kernel on low-bit-activity inputs (sparse, zero Q) with power "
+                         "and clock samples (reported under 'input_study')")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
                     help="after timing, run one device-to-device copy of this many MiB "
                          "(a known-size kernel for scaling HBM byte counters)")
     return ap.parse_args()
+
+
+def _dpm_current_mhz(path):
+    """The level marked '*' in an amdgpu pp_dpm_sclk table, in MHz (None if unreadable)."""
+    try:
+        for ln in open(path):
+            if ln.rstrip().endswith("*"):
+                v = ln.split(":", 1)[1].strip().rstrip("*").strip().lower()
+                return float(v.replace("mhz", ""))
+    except Exception:
+        pass
+    return None
 
 
 def sclk_mhz():
@@ -51,14 +66,96 @@ def sclk_mhz():
     Read from a file: no helper program is started after the GPU is initialised."""
     import glob
     for path in sorted(glob.glob("/sys/class/drm/card*/device/pp_dpm_sclk")):
-        try:
-            for ln in open(path):
-                if ln.rstrip().endswith("*"):
-                    v = ln.split(":", 1)[1].strip().rstrip("*").strip().lower()
-                    return float(v.replace("mhz", ""))
-        except Exception:
-            continue
+        v = _dpm_current_mhz(path)
+        if v is not None:
+            return v
     return None
+
+
+def _gpu_hwmon_dirs():
+    """sysfs device directories of the DRM cards whose PCI address is torch's cuda:0 (or, failing
+    that, of the only card with a DPM clock table).  Read-only file access."""
+    import glob
+    cards = [c for c in sorted(glob.glob("/sys/class/drm/card*/device")) if os.path.exists(c + "/pp_dpm_sclk")]
+    try:
+        import torch
+        pr = torch.cuda.get_device_properties(0)
+        want = f"{pr.pci_domain_id:04x}:{pr.pci_bus_id:02x}:{pr.pci_device_id:02x}"
+        match = [c for c in cards if os.path.basename(os.path.realpath(c)).startswith(want)]
+        if match:
+            return match[:1]
+    except Exception:
+        pass
+    return cards if len(cards) == 1 else []
+
+
+class PowerClockSampler:
+    """Samples the GPU's board power and shader clock from sysfs hwmon in a background thread
+    while the timed launches run (file reads only; nothing is executed)."""
+
+    def __init__(self, period_s=0.002):
+        import glob
+        self.period = period_s
+        self.power_file, self.clock_file, self.dpm_file, self.power_cap_w = None, None, None, None
+        for dev in _gpu_hwmon_dirs():
+            for hw in sorted(glob.glob(dev + "/hwmon/hwmon*")):
+                for name in ("power1_average", "power1_input"):
+                    if self.power_file is None and os.path.exists(f"{hw}/{name}"):
+                        self.power_file = f"{hw}/{name}"
+                if os.path.exists(f"{hw}/freq1_input"):
+                    self.clock_file = f"{hw}/freq1_input"
+                cap = self._read(f"{hw}/power1_cap")
+                if cap is not None:
+                    self.power_cap_w = cap * 1e-6
+            if self.clock_file is None and os.path.exists(dev + "/pp_dpm_sclk"):
+                self.dpm_file = dev + "/pp_dpm_sclk"     # current DPM level, marked '*'
+        self.power, self.clock = [], []
+        self._stop = None
+        self._thread = None
+
+    @staticmethod
+    def _read(path):
+        try:
+            with open(path) as f:
+                return float(f.read().strip())
+        except Exception:
+            return None
+
+    def _run(self):
+        while not self._stop.is_set():
+            if self.power_file:
+                v = self._read(self.power_file)
+                if v is not None:
+                    self.power.append(v * 1e-6)          # microwatts -> W
+            if self.clock_file:
+                v = self._read(self.clock_file)
+                if v is not None:
+                    self.clock.append(v * 1e-6)          # Hz -> MHz
+            elif self.dpm_file:
+                v = _dpm_current_mhz(self.dpm_file)
+                if v is not None:
+                    self.clock.append(v)
+            self._stop.wait(self.period)
+
+    def __enter__(self):
+        import threading
+        self.power, self.clock = [], []
+        self._stop = threading.Event()
+        self._thread = threading.Thread(target=self._run, daemon=True)
+        self._thread.start()
+        return self
+
+    def __exit__(self, *exc):
+        self._stop.set()
+        self._thread.join()
+
+    def summary(self, flop, seconds):
+        """Average power (W), shader clock (MHz), and FLOP per joule over the sampled window."""
+        p = sum(self.power) / len(self.power) if self.power else None
+        c = sum(self.clock) / len(self.clock) if self.clock else None
+        return {"power_w_avg": p, "power_cap_w": self.power_cap_w, "sclk_mhz_avg": c,
+                "samples": len(self.power), "tflop_per_joule": (flop / (p * seconds) / 1e12) if p else None,
+                "power_source": self.power_file, "clock_source": self.clock_file or self.dpm_file}
 
 
 def measured_traffic(workload, mode):
@@ -78,20 +175,22 @@ def measured_traffic(workload, mode):
     return t["hbm_read_bytes_per_launch"] + t["hbm_write_bytes_per_launch"]
 
 
-def time_launches(fn, steps, warmup, stream):
+def time_launches(fn, steps, warmup, stream, sampler=None):
+    import contextlib
     import torch
     for _ in range(warmup):
         fn()
     torch.cuda.synchronize()
     starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
     ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
-    t0 = time.perf_counter()
-    for i in range(steps):
-        starts[i].record(stream)
-        fn()
-        ends[i].record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
+    with sampler if sampler is not None else contextlib.nullcontext():
+        t0 = time.perf_counter()
+        for i in range(steps):
+            starts[i].record(stream)
+            fn()
+            ends[i].record(stream)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
     per = sorted(s.elapsed_time(e) for s, e in zip(starts, ends))   # ms, HIP events on the launch stream
     return wall, per
 
@@ -127,6 +226,44 @@ def rotate_quant_timing(w, steps, warmup, stream, attn_ms):
             "ms_q_plus_k": total_ms, "fraction_of_attention_time": total_ms / attn_ms,
             "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                          "frac": achieved / HBM_PEAK_GBPS, "traffic": None}}
+
+
+def sparse_codes(x, frac=0.9, sample=1 << 20):
+    """e4m3 codes x (uint8 tensor, any device) with every code whose magnitude is below the
+    `frac` quantile of |code| set to +0.  The quantile comes from an evenly strided sample taken
+    as a strided view (no index tensor), moved to the host."""
+    import torch
+    flat = x.reshape(-1)
+    picked = (flat[:: max(1, flat.numel() // sample)] & 0x7F).cpu().float()
+    thr = torch.kthvalue(picked, max(1, int(frac * picked.numel()))).values.item()
+    return torch.where((x & 0x7F) < thr, torch.zeros_like(x), x)
+
+
+def input_study(w, d, q, k, v, out, stream, flops, steps, warmup, modes, paths):
+    """Throughput, shader clock, power and TFLOP/J of the FP8 kernel on inputs with less operand
+    bit activity than Gaussian ones (the pages: the sustained clock depends on how many operand
+    bits flip).  Same shapes, same FLOP count, same kernel:
+      gaussian - the workload itself (from `paths`);
+      sparse90 - Q, K and V codes of magnitude below each tensor's 90th percentile set to +0;
+      zero_q   - Q = 0: every score is 0, so every probability byte is the same (e4m3 256)."""
+    import torch
+    from fp8_causal_prefill_tiled_amd import binding
+
+    variants = {"sparse90": (sparse_codes(q), sparse_codes(k), sparse_codes(v)),
+                "zero_q": (torch.zeros_like(q), k, v)}
+    res = {"gaussian": {m: {"tflops": paths[m]["tflops"], **paths[m]["energy"]} for m in modes}}
+    sampler = PowerClockSampler()
+    for name, (qq, kk, vv) in variants.items():
+        res[name] = {}
+        for mode in modes:
+            def fn():
+                binding.attn_fwd_fp8(qq, kk, vv, d["q_scale"], d["k_scale"], d["v_scale"], p_mode=mode, out=out,
+                                     stream=stream)
+            wall, per = time_launches(fn, steps, warmup, stream, sampler)
+            res[name][mode] = {"tflops": flops * steps / wall / 1e12, **sampler.summary(flops * steps, wall)}
+        del qq
+    torch.cuda.synchronize()
+    return res
 
 
 def cpu_baseline(w, d, out_gpu, seconds, dtype):
@@ -230,8 +367,9 @@ def main():
 
     paths = {}
     clk_before = sclk_mhz()
+    sampler = PowerClockSampler()
     for mode in reversed(modes):          # headline mode last: its output stays in `out`
-        wall, per = time_launches(make_fn(mode), args.steps, args.warmup, stream)
+        wall, per = time_launches(make_fn(mode), args.steps, args.warmup, stream, sampler)
         avg_ms = sum(per) / len(per)
         paths[mode] = {
             "tflops": flops * args.steps / wall / 1e12,
@@ -239,8 +377,12 @@ def main():
             "kernel_ms_avg": avg_ms, "kernel_ms_median": per[len(per) // 2],
             "kernel_ms_min": per[0], "kernel_ms_max": per[-1],
             "frac_of_peak": flops / (avg_ms * 1e-3) / 1e12 / peak,
+            "energy": sampler.summary(flops * args.steps, wall),
         }
     clk_after = sclk_mhz()
+    study = None
+    if args.input_study and args.dtype == "fp8":
+        study = input_study(w, d, q, k, v, out, stream, flops, args.steps, args.warmup, modes, paths)
     if args.calibrate_copy_mib:
         n = args.calibrate_copy_mib << 20
         src = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
@@ -287,6 +429,7 @@ def main():
                      "kernel": f"{args.dtype}_causal_fwd", "per_launch_tflop": flops / 1e12},
         "paths": paths,
         "rotate_quant": rot,
+        "input_study": study,
         "sclk_mhz": {"before": clk_before, "after": clk_after},
         "cpu_baseline": cpu,
     }
