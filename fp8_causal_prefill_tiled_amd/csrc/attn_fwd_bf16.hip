@@ -178,7 +178,9 @@ __global__ void __launch_bounds__(512) bf16_causal_fwd(Bf16Params a) {
     // Every block index is loaded (blocks past the last one read zeros through an
     // empty range), so the staging steps need no guards.
     auto gload = [&](int j) {
-        const int rows = max(min(S - j * KB, KB), 0);
+        // rows of block j inside the tensor, clamped to [0, KB]; uniform, so kept on the
+        // scalar unit (a fused vector med3 would cost three vector instructions per block)
+        const int rows = min(__builtin_amdgcn_readfirstlane(max(S - j * KB, 0)), KB);
         if (grp == 0) {
             const auto r = buffer_rsrc(kbase + (int64_t)j * KB * k_row, rows * k_row);
 #pragma unroll
@@ -275,7 +277,7 @@ __global__ void __launch_bounds__(512) bf16_causal_fwd(Bf16Params a) {
         for (int r = r0; r < r1; ++r) mx_n = fmaxf(fmaxf(mx_n, s0[r]), s1[r]);
     };
     auto prep_ref = [&]() {
-        const float mx = fmaxf(mx_n, other_half(mx_n));
+        const float mx = pair_max(mx_n);
         const float M = fmaxf(ceilf(mx * a.c), -1.0e30f);   // floor: rows with no visible key here
         need_n = M > ref + kRefSlack;
         nref_n = need_n ? M : ref;

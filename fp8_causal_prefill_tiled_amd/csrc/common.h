@@ -27,6 +27,15 @@ __device__ __forceinline__ float other_half(float x) {
     return __int_as_float((threadIdx.x & 32) ? r[0] : r[1]);
 }
 
+// max of x over the lane pair (l, l ^ 32).  v_permlane32_swap of x with itself
+// leaves the lower half's 32 values in one result and the upper half's in the
+// other, each in every lane, so one max of the two covers both lanes of a pair.
+__device__ __forceinline__ float pair_max(float x) {
+    const int xi = __float_as_int(x);
+    const auto r = __builtin_amdgcn_permlane32_swap(xi, xi, false, false);
+    return fmaxf(__int_as_float(r[0]), __int_as_float(r[1]));
+}
+
 __device__ __forceinline__ i32x4 load16(const void* p) {
     return *reinterpret_cast<const i32x4*>(p);
 }
