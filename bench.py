@@ -306,8 +306,10 @@ def cpu_baseline(w, d, out_gpu, seconds, dtype):
             got = out_gpu[:, rows, h:h + 1].astype(np.float64)
             errs_num += float(np.sum((got - ref) ** 2))
             errs_den += float(np.sum(ref ** 2))
+    tiny = _cpu_tiny_full()
     return {
         "value": flops / el / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+        "tiny_full": tiny,
         "sample": f"fp64 attention (oracle/attention64.py, numpy+BLAS) on {nrows} query rows "
                   f"(spread over 0..S-1, longest prefixes first) x heads {heads} of the {w.name} workload, "
                   f"{el:.1f} s of oracle time; FLOPs counted 2*(i+1)*(d_qk+d_v) per row i",
@@ -315,6 +317,30 @@ def cpu_baseline(w, d, out_gpu, seconds, dtype):
         "cpu_model": _cpu_model(),
         "os_cpu_count": os.cpu_count(),
     }
+
+
+def _cpu_tiny_full():
+    """The oracle on the whole tiny workload (B=1, H=2, S=256, d=128, FP8 inputs dequantised), on
+    all threads and on one thread; best of three runs each, TFLOP/s by the causal formula."""
+    from threadpoolctl import threadpool_limits
+    from oracle.attention64 import attention_fp64, dequantize
+    from fp8_causal_prefill_tiled_amd import workloads as W
+    tw = W.WORKLOADS["tiny"]
+    td = W.make_fp8(tw)
+    q, k, v = (dequantize(td[n + "8"].numpy(), td[n + "_scale"]) for n in ("q", "k", "v"))
+
+    def best():
+        ts = []
+        for _ in range(3):
+            t0 = time.perf_counter()
+            attention_fp64(q, k, v)
+            ts.append(time.perf_counter() - t0)
+        return min(ts)
+    t_all = best()
+    with threadpool_limits(limits=1):
+        t_one = best()
+    return {"workload": "tiny (B=1, Hq=Hkv=2, S=256, d=128)", "all_threads_tflops": tw.causal_flops / t_all / 1e12,
+            "one_thread_tflops": tw.causal_flops / t_one / 1e12, "all_threads_s": t_all, "one_thread_s": t_one}
 
 
 def _cpu_model():
