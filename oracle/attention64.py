@@ -21,6 +21,12 @@ key/value head floor(h / (Hq / Hkv)) (consecutive groups, the flash_attn
 convention behind the "drop-in flash_attn_func interface", [MTP] §TL;DR);
 tensors are (B, S, H, d), contiguous in d.
 
+Unequal query and key lengths (Sq queries, Sk keys; outside the pages' scope, for
+chunked prefill and variable-length batches): reading - the causal mask is aligned
+at the bottom right, as in FlashAttention 2.1 and later, so query i sees keys
+j <= i + (Sk - Sq); a query that sees no key gets O = 0 and a log-sum-exp of -inf.
+With Sq == Sk this is the causal mask above.
+
 Every query row is computed independently from the definition; rows are only
 grouped into chunks to bound memory.
 """
@@ -45,25 +51,35 @@ def _rows_of(rows, S):
     return np.asarray(rows, dtype=np.int64)
 
 
+def visible_keys(rows, Sq, Sk, causal):
+    """Number of keys each query row sees: keys 0 .. n-1 with n = clip(i + 1 + Sk - Sq, 0, Sk)
+    when causal (bottom-right aligned), all Sk keys otherwise."""
+    rows = np.asarray(rows, dtype=np.int64)
+    if not causal:
+        return np.full(rows.shape, Sk, dtype=np.int64)
+    return np.clip(rows + 1 + (Sk - Sq), 0, Sk)
+
+
 def attention_fp64(q, k, v, sm_scale=None, causal=True, rows=None, chunk=512):
     """Causal (or full) softmax attention in fp64.
 
-    q: (B, S, Hq, d_qk), k: (B, S, Hkv, d_qk), v: (B, S, Hkv, d_v), any real dtype.
+    q: (B, Sq, Hq, d_qk), k: (B, Sk, Hkv, d_qk), v: (B, Sk, Hkv, d_v), any real dtype
+    (Sq == Sk for the pages' equal-length case).
     rows: optional 1-D array of query positions to evaluate (default: all).
     Returns O of shape (B, len(rows), Hq, d_v), float64.
     """
     q = np.asarray(q, dtype=np.float64)
     k = np.asarray(k, dtype=np.float64)
     v = np.asarray(v, dtype=np.float64)
-    B, S, Hq, dqk = q.shape
-    Hkv = k.shape[2]
+    B, Sq, Hq, dqk = q.shape
+    Sk, Hkv = k.shape[1], k.shape[2]
     dv = v.shape[3]
-    assert k.shape == (B, S, Hkv, dqk) and v.shape == (B, S, Hkv, dv)
+    assert k.shape == (B, Sk, Hkv, dqk) and v.shape == (B, Sk, Hkv, dv)
     assert Hq % Hkv == 0
     sm = 1.0 / np.sqrt(dqk) if sm_scale is None else float(sm_scale)
-    rows = _rows_of(rows, S)
-    out = np.empty((B, len(rows), Hq, dv), dtype=np.float64)
-    keys = np.arange(S)
+    rows = _rows_of(rows, Sq)
+    out = np.zeros((B, len(rows), Hq, dv), dtype=np.float64)
+    keys = np.arange(Sk)
     for b in range(B):
         for h in range(Hq):
             g = kv_head(h, Hq, Hkv)
@@ -71,40 +87,47 @@ def attention_fp64(q, k, v, sm_scale=None, causal=True, rows=None, chunk=512):
             vv = v[b, :, g, :]
             for c0 in range(0, len(rows), chunk):
                 r = rows[c0:c0 + chunk]
-                n = (int(r.max()) + 1) if causal else S  # keys any row here can see
-                logits = sm * (q[b, r, h, :] @ kk[:n].T)
-                if causal:
-                    logits = np.where(keys[None, :n] <= r[:, None], logits, -np.inf)
+                nvis = visible_keys(r, Sq, Sk, causal)
+                n = int(nvis.max())                    # keys any row here can see
+                live = nvis > 0                        # rows that see no key keep O = 0
+                if n == 0:
+                    continue
+                logits = sm * (q[b, r[live], h, :] @ kk[:n].T)
+                logits = np.where(keys[None, :n] < nvis[live][:, None], logits, -np.inf)
                 m = logits.max(axis=1, keepdims=True)
                 w = np.exp(logits - m)
                 w /= w.sum(axis=1, keepdims=True)
-                out[b, c0:c0 + len(r), h, :] = w @ vv[:n]
+                out[b, c0 + np.flatnonzero(live), h, :] = w @ vv[:n]
     return out
 
 
 def lse_fp64(q, k, sm_scale=None, causal=True, rows=None, chunk=512):
     """Natural-log softmax normaliser of each query row, ln sum_j exp(sm <q_i, k_j>) over
-    the keys the row sees (all keys, or j <= i when causal), in fp64.  Returns
-    (B, Hq, len(rows)): the layout attention libraries return it in."""
+    the keys the row sees (all keys, or the causal ones as in attention_fp64), in fp64;
+    -inf for a row that sees no key.  Returns (B, Hq, len(rows)): the layout attention
+    libraries return it in."""
     q = np.asarray(q, dtype=np.float64)
     k = np.asarray(k, dtype=np.float64)
-    B, S, Hq, dqk = q.shape
-    Hkv = k.shape[2]
+    B, Sq, Hq, dqk = q.shape
+    Sk, Hkv = k.shape[1], k.shape[2]
     sm = 1.0 / np.sqrt(dqk) if sm_scale is None else float(sm_scale)
-    rows = _rows_of(rows, S)
-    out = np.empty((B, Hq, len(rows)), dtype=np.float64)
-    keys = np.arange(S)
+    rows = _rows_of(rows, Sq)
+    out = np.full((B, Hq, len(rows)), -np.inf, dtype=np.float64)
+    keys = np.arange(Sk)
     for b in range(B):
         for h in range(Hq):
             kk = k[b, :, kv_head(h, Hq, Hkv), :]
             for c0 in range(0, len(rows), chunk):
                 r = rows[c0:c0 + chunk]
-                n = (int(r.max()) + 1) if causal else S
-                logits = sm * (q[b, r, h, :] @ kk[:n].T)
-                if causal:
-                    logits = np.where(keys[None, :n] <= r[:, None], logits, -np.inf)
+                nvis = visible_keys(r, Sq, Sk, causal)
+                n = int(nvis.max())
+                live = nvis > 0
+                if n == 0:
+                    continue
+                logits = sm * (q[b, r[live], h, :] @ kk[:n].T)
+                logits = np.where(keys[None, :n] < nvis[live][:, None], logits, -np.inf)
                 m = logits.max(axis=1)
-                out[b, h, c0:c0 + len(r)] = m + np.log(np.exp(logits - m[:, None]).sum(axis=1))
+                out[b, h, c0 + np.flatnonzero(live)] = m + np.log(np.exp(logits - m[:, None]).sum(axis=1))
     return out
 
 

@@ -47,7 +47,7 @@ result is then the plain definition, which pins this module to
 import numpy as np
 
 from .e4m3 import decode_e4m3, encode_e4m3_rne, round_to_e4m3
-from .attention64 import kv_head, _rows_of
+from .attention64 import kv_head, visible_keys, _rows_of
 
 LOG2E = 1.4426950408889634
 BLOCK_KEYS = 64
@@ -84,7 +84,9 @@ def _block_probs(t, valid, p_mode, rounding, s=None, A=None):
 
 def emulate_fp8(q8, k8, v8, q_scale, k_scale, v_scale, sm_scale=None, p_mode="exact",
                 causal=True, rows=None, rounding=True, chunk=256, return_lse=False):
-    """Emulate the FP8 method on e4m3 codes (uint8 arrays, (B, S, H, d) layout).
+    """Emulate the FP8 method on e4m3 codes (uint8 arrays, (B, S, H, d) layout; K and V may
+    have their own length Sk, with the causal mask and the no-key convention of
+    attention64.attention_fp64).
 
     Returns O (B, len(rows), Hq, d_v) float64.  With ``return_lse`` also returns
     log2L (B, len(rows), Hq) = log2(sum_b 2^(M_ib - 8) l_ib), the base-2 log of the
@@ -96,14 +98,14 @@ def emulate_fp8(q8, k8, v8, q_scale, k_scale, v_scale, sm_scale=None, p_mode="ex
     k8 = np.asarray(k8, dtype=np.uint8)
     v8 = np.asarray(v8, dtype=np.uint8)
     B, S, Hq, dqk = q8.shape
-    Hkv = k8.shape[2]
+    Sk, Hkv = k8.shape[1], k8.shape[2]
     dv = v8.shape[3]
     sm = 1.0 / np.sqrt(dqk) if sm_scale is None else float(sm_scale)
     C = float(q_scale) * float(k_scale) * sm * LOG2E
     A = np.float64(np.float32(8.0 * C))
     rows = _rows_of(rows, S)
-    out = np.empty((B, len(rows), Hq, dv))
-    log2L = np.empty((B, len(rows), Hq))
+    out = np.zeros((B, len(rows), Hq, dv))
+    log2L = np.full((B, len(rows), Hq), -np.inf)
     qd = decode_e4m3(q8)
     kd = decode_e4m3(k8)
     vd = decode_e4m3(v8)
@@ -111,16 +113,19 @@ def emulate_fp8(q8, k8, v8, q_scale, k_scale, v_scale, sm_scale=None, p_mode="ex
         for h in range(Hq):
             g = kv_head(h, Hq, Hkv)
             for c0 in range(0, len(rows), chunk):
-                r = rows[c0:c0 + chunk]
-                n = (int(r.max()) + 1) if causal else S
+                r_all = rows[c0:c0 + chunk]
+                nvis_all = visible_keys(r_all, S, Sk, causal)
+                live = np.flatnonzero(nvis_all > 0)       # rows that see no key keep O = 0
+                if len(live) == 0:
+                    continue
+                r, nvis = r_all[live], nvis_all[live]
+                n = int(nvis.max())
                 nb = (n + BLOCK_KEYS - 1) // BLOCK_KEYS
                 npad = nb * BLOCK_KEYS
                 s = np.zeros((len(r), npad))
                 s[:, :n] = qd[b, r, h, :] @ kd[b, :n, g, :].T
                 keys = np.arange(npad)
-                valid = np.broadcast_to(keys[None, :] < n, (len(r), npad))
-                if causal:
-                    valid = valid & (keys[None, :] <= r[:, None])
+                valid = keys[None, :] < nvis[:, None]
                 s3 = s.reshape(len(r), nb, BLOCK_KEYS)
                 v3 = valid.reshape(len(r), nb, BLOCK_KEYS)
                 p, M, has = _block_probs(s3 * C, v3, p_mode, rounding, s=s3, A=A)
@@ -130,8 +135,8 @@ def emulate_fp8(q8, k8, v8, q_scale, k_scale, v_scale, sm_scale=None, p_mode="ex
                 den = (fac * l).sum(axis=1)
                 W = (p * fac[:, :, None]).reshape(len(r), npad)[:, :n]
                 num = W @ vd[b, :n, g, :]
-                out[b, c0:c0 + len(r), h, :] = float(v_scale) * (num / den[:, None])
-                log2L[b, c0:c0 + len(r), h] = np.log2(den) + Rref - 8.0
+                out[b, c0 + live, h, :] = float(v_scale) * (num / den[:, None])
+                log2L[b, c0 + live, h] = np.log2(den) + Rref - 8.0
     if return_lse:
         return out, log2L
     return out

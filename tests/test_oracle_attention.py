@@ -133,3 +133,62 @@ def test_lse_closed_forms():
     z = lse_fp64(np.zeros_like(q), k)
     assert np.allclose(z[0, 0], np.log(np.arange(1, 7)), atol=1e-14)
     assert np.allclose(lse_fp64(np.zeros_like(q), k, causal=False), np.log(6.0), atol=1e-14)
+
+
+# ------------------------------------------------- unequal query and key lengths
+
+def brute_force_unequal(q, k, v, sm, causal):
+    """Pure-Python loops: query i of Sq sees keys j <= i + Sk - Sq (causal) or all Sk keys;
+    a query that sees no key gets 0 and a log-sum-exp of -inf."""
+    B, Sq, Hq, dqk = q.shape
+    Sk, Hkv = k.shape[1], k.shape[2]
+    out = np.zeros((B, Sq, Hq, v.shape[3]))
+    lse = np.full((B, Hq, Sq), -np.inf)
+    for b in range(B):
+        for h in range(Hq):
+            g = h // (Hq // Hkv)
+            for i in range(Sq):
+                js = [j for j in range(Sk) if (not causal) or j <= i + Sk - Sq]
+                if not js:
+                    continue
+                logits = [sm * sum(float(q[b, i, h, c]) * float(k[b, j, g, c]) for c in range(dqk)) for j in js]
+                m = max(logits)
+                e = [math.exp(x - m) for x in logits]
+                tot = sum(e)
+                lse[b, h, i] = m + math.log(tot)
+                for c in range(v.shape[3]):
+                    out[b, i, h, c] = sum(e[t] * float(v[b, j, g, c]) for t, j in enumerate(js)) / tot
+    return out, lse
+
+
+@pytest.mark.parametrize("causal", [True, False])
+@pytest.mark.parametrize("Sq,Sk", [(5, 12), (12, 5), (7, 7), (1, 9)])
+def test_unequal_lengths_match_brute_force(Sq, Sk, causal):
+    rng = np.random.default_rng(Sq * 31 + Sk)
+    q = rng.standard_normal((1, Sq, 4, 6))
+    k = rng.standard_normal((1, Sk, 2, 6))
+    v = rng.standard_normal((1, Sk, 2, 3))
+    ref_o, ref_l = brute_force_unequal(q, k, v, 0.7, causal)
+    o = attention_fp64(q, k, v, sm_scale=0.7, causal=causal, chunk=4)
+    l = lse_fp64(q, k, sm_scale=0.7, causal=causal, chunk=4)
+    assert np.max(np.abs(o - ref_o)) < 1e-12
+    assert np.array_equal(np.isinf(l), np.isinf(ref_l))
+    fin = np.isfinite(ref_l)
+    assert np.max(np.abs(l[fin] - ref_l[fin])) < 1e-12
+
+
+def test_unequal_causal_is_the_tail_of_the_full_problem():
+    # Bottom-right alignment: Sq queries against Sk >= Sq keys are the last Sq rows of the
+    # equal-length causal problem, whatever the earlier query rows hold.
+    rng = np.random.default_rng(8)
+    Sk, Sq = 40, 13
+    qf = rng.standard_normal((2, Sk, 4, 8))
+    k = rng.standard_normal((2, Sk, 2, 8))
+    v = rng.standard_normal((2, Sk, 2, 8))
+    full = attention_fp64(qf, k, v)
+    tail = attention_fp64(qf[:, Sk - Sq:], k, v)
+    assert np.max(np.abs(tail - full[:, Sk - Sq:])) < 1e-13
+    assert np.max(np.abs(lse_fp64(qf[:, Sk - Sq:], k) - lse_fp64(qf, k)[:, :, Sk - Sq:])) < 1e-12
+    # more queries than keys: the first Sq - Sk rows see nothing
+    o = attention_fp64(rng.standard_normal((1, 9, 2, 8)), k[:1, :4], v[:1, :4])
+    assert np.all(o[:, :5] == 0) and np.all(np.abs(o[:, 5:]) > 0)

@@ -166,3 +166,36 @@ def test_lse_of_rounded_weights_within_the_probability_bounds(p_mode, lo, hi, ca
     assert d.min() >= np.log(lo) - 2.0 ** -7 and d.max() <= np.log(hi) + 2.0 ** -7
     # the rounding is visible (the bound is not vacuous) and mostly averages out over a row
     assert np.abs(d).max() > 1e-4 and np.abs(d).mean() < 0.05
+
+
+# ------------------------------------------------- unequal query and key lengths
+
+@pytest.mark.parametrize("causal", [True, False])
+@pytest.mark.parametrize("Sq,Sk", [(70, 200), (200, 70), (1, 129)])
+def test_unequal_lengths_without_rounding_is_the_plain_definition(Sq, Sk, causal):
+    rng = np.random.default_rng(Sq + 7 * Sk)
+    q8, qs = _codes((1, Sq, 4, 32), rng, 2.0)
+    k8, ks = _codes((1, Sk, 2, 32), rng)
+    v8, vs = _codes((1, Sk, 2, 16), rng)
+    qd, kd, vd = dequantize(q8, qs), dequantize(k8, ks), dequantize(v8, vs)
+    emu, log2L = emulate_fp8(q8, k8, v8, qs, ks, vs, rounding=False, causal=causal, return_lse=True, chunk=48)
+    assert np.max(np.abs(emu - attention_fp64(qd, kd, vd, causal=causal))) < 1e-12
+    ref = lse_fp64(qd, kd, causal=causal)
+    got = np.log(2.0) * log2L.transpose(0, 2, 1)
+    assert np.array_equal(np.isinf(got), np.isinf(ref))
+    fin = np.isfinite(ref)
+    assert np.max(np.abs(got[fin] - ref[fin])) < 1e-12
+
+
+@pytest.mark.parametrize("p_mode", ["exact", "lean"])
+def test_unequal_causal_emulation_is_the_tail_of_the_full_problem(p_mode):
+    # the rounded method too: each row's blocks, exponents and rounded probabilities are the same
+    rng = np.random.default_rng(12)
+    Sk, Sq = 300, 77
+    q8, qs = _codes((1, Sk, 2, 64), rng, 2.0)
+    k8, ks = _codes((1, Sk, 1, 64), rng)
+    v8, vs = _codes((1, Sk, 1, 32), rng)
+    full, lf = emulate_fp8(q8, k8, v8, qs, ks, vs, p_mode=p_mode, return_lse=True)
+    tail, lt = emulate_fp8(q8[:, Sk - Sq:], k8, v8, qs, ks, vs, p_mode=p_mode, return_lse=True)
+    assert np.max(np.abs(tail - full[:, Sk - Sq:])) <= 1e-13 * np.max(np.abs(full))
+    assert np.max(np.abs(lt - lf[:, Sk - Sq:])) < 1e-12
