@@ -53,9 +53,9 @@ def load_library():
     lib.attn_fwd_bf16.restype = i
     lib.attn_fwd_bf16_lse.argtypes = [vp, vp, vp, vp, vp, f, i, i, i, i, i, i, i, vp]
     lib.attn_fwd_bf16_lse.restype = i
-    lib.attn_fwd_fp8_varlen.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, f, f, f, f, i, i, i, i, i, i, vp]
+    lib.attn_fwd_fp8_varlen.argtypes = [vp, vp, vp, vp, vp, vp, vp, i, i, i, i, f, f, f, f, i, i, i, i, i, i, vp]
     lib.attn_fwd_fp8_varlen.restype = i
-    lib.attn_fwd_bf16_varlen.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, f, i, i, i, i, i, vp]
+    lib.attn_fwd_bf16_varlen.argtypes = [vp, vp, vp, vp, vp, vp, vp, i, i, i, i, f, i, i, i, i, i, vp]
     lib.attn_fwd_bf16_varlen.restype = i
     lib.attn_rotate_quant_bf16.argtypes = [vp, vp, vp, i, i, i, i, vp]
     lib.attn_rotate_quant_bf16.restype = i
@@ -120,17 +120,17 @@ def attn_fwd_bf16_lse_raw(q, k, v, o, lse, softmax_scale, B, Hq, Hkv, S, d_qk, d
                                             stream)
 
 
-def attn_fwd_fp8_varlen_raw(q, k, v, o, lse, cu_seqlens, n_seqs, max_seqlen, total_tokens, q_scale, k_scale, v_scale,
-                            softmax_scale, Hq, Hkv, d_qk, d_v, causal, p_mode, stream=0):
-    return load_library().attn_fwd_fp8_varlen(q, k, v, o, lse, cu_seqlens, n_seqs, max_seqlen, total_tokens,
-                                              q_scale, k_scale, v_scale, softmax_scale, Hq, Hkv, d_qk, d_v,
-                                              causal, p_mode, stream)
+def attn_fwd_fp8_varlen_raw(q, k, v, o, lse, cu_seqlens_q, cu_seqlens_k, n_seqs, max_seqlen_q, total_q, total_k,
+                            q_scale, k_scale, v_scale, softmax_scale, Hq, Hkv, d_qk, d_v, causal, p_mode, stream=0):
+    return load_library().attn_fwd_fp8_varlen(q, k, v, o, lse, cu_seqlens_q, cu_seqlens_k, n_seqs, max_seqlen_q,
+                                              total_q, total_k, q_scale, k_scale, v_scale, softmax_scale, Hq, Hkv,
+                                              d_qk, d_v, causal, p_mode, stream)
 
 
-def attn_fwd_bf16_varlen_raw(q, k, v, o, lse, cu_seqlens, n_seqs, max_seqlen, total_tokens, softmax_scale,
-                             Hq, Hkv, d_qk, d_v, causal, stream=0):
-    return load_library().attn_fwd_bf16_varlen(q, k, v, o, lse, cu_seqlens, n_seqs, max_seqlen, total_tokens,
-                                               softmax_scale, Hq, Hkv, d_qk, d_v, causal, stream)
+def attn_fwd_bf16_varlen_raw(q, k, v, o, lse, cu_seqlens_q, cu_seqlens_k, n_seqs, max_seqlen_q, total_q, total_k,
+                             softmax_scale, Hq, Hkv, d_qk, d_v, causal, stream=0):
+    return load_library().attn_fwd_bf16_varlen(q, k, v, o, lse, cu_seqlens_q, cu_seqlens_k, n_seqs, max_seqlen_q,
+                                               total_q, total_k, softmax_scale, Hq, Hkv, d_qk, d_v, causal, stream)
 
 
 def attn_rotate_quant_bf16_raw(x, x8, scale, B, S, H, d, stream=0):
@@ -234,52 +234,62 @@ def _thd(x, name):
     return x.shape
 
 
-def _varlen_common(q, k, v, cu_seqlens, out, return_lse):
+def _check_cu(cu, name):
+    if cu.dtype != torch.int32 or cu.dim() != 1 or not cu.is_cuda or not cu.is_contiguous() or cu.numel() < 1:
+        raise ValueError(f"{name} must be a contiguous 1-D int32 GPU tensor of n_seqs + 1 offsets")
+
+
+def _varlen_common(q, k, v, cu_seqlens, out, return_lse, cu_seqlens_k=None):
     T, Hq, dqk = _thd(q, "q")
     Tk, Hkv, dk = _thd(k, "k")
     Tv, Hv, dv = _thd(v, "v")
-    if (Tk, dk) != (T, dqk) or (Tv, Hv) != (T, Hkv):
+    if dk != dqk or (Tv, Hv) != (Tk, Hkv) or (cu_seqlens_k is None and Tk != T):
         raise ValueError(f"shape mismatch q{tuple(q.shape)} k{tuple(k.shape)} v{tuple(v.shape)}")
-    if cu_seqlens.dtype != torch.int32 or cu_seqlens.dim() != 1 or not cu_seqlens.is_cuda \
-            or not cu_seqlens.is_contiguous() or cu_seqlens.numel() < 1:
-        raise ValueError("cu_seqlens must be a contiguous 1-D int32 GPU tensor of n_seqs + 1 offsets")
+    _check_cu(cu_seqlens, "cu_seqlens")
+    if cu_seqlens_k is not None:
+        _check_cu(cu_seqlens_k, "cu_seqlens_k")
+        if cu_seqlens_k.numel() != cu_seqlens.numel():
+            raise ValueError("cu_seqlens and cu_seqlens_k must hold the same number of offsets")
     if out is None:
         out = torch.empty((T, Hq, dv), dtype=torch.bfloat16, device=q.device)
     elif out.dtype != torch.bfloat16 or tuple(out.shape) != (T, Hq, dv) or not out.is_contiguous():
         raise ValueError("out must be a contiguous bf16 tensor of shape (total_tokens, Hq, d_v)")
     lse = torch.empty((Hq, T), dtype=torch.float32, device=q.device) if return_lse else None
-    return T, Hq, Hkv, dqk, dv, out, lse
+    return T, Tk, Hq, Hkv, dqk, dv, out, lse
 
 
 def attn_fwd_fp8_varlen(q8, k8, v8, cu_seqlens, max_seqlen, q_scale, k_scale, v_scale, softmax_scale=None,
-                        causal=True, p_mode="exact", out=None, stream=None, return_lse=False):
-    """FP8 attention over a variable-length batch packed along the rows: q8 (total, Hq, d_qk),
-    k8/v8 (total, Hkv, d), sequence i at rows cu_seqlens[i]..cu_seqlens[i+1]-1 (int32 GPU tensor),
-    max_seqlen the longest length (host int).  Returns bf16 (total, Hq, d_v), or (out, lse) with
-    lse fp32 (Hq, total)."""
+                        causal=True, p_mode="exact", out=None, stream=None, return_lse=False, cu_seqlens_k=None):
+    """FP8 attention over a variable-length batch packed along the rows: q8 (total_q, Hq, d_qk),
+    k8/v8 (total_k, Hkv, d), sequence i's queries at rows cu_seqlens[i]..cu_seqlens[i+1]-1 (int32
+    GPU tensor) and its keys at the same rows of k8/v8, or at cu_seqlens_k's rows when given
+    (bottom-right aligned causal mask when the lengths differ); max_seqlen is the longest query
+    run (host int).  Returns bf16 (total_q, Hq, d_v), or (out, lse) with lse fp32 (Hq, total_q)."""
     for t, n in ((q8, "q8"), (k8, "k8"), (v8, "v8")):
         if t.dtype not in (torch.uint8, torch.float8_e4m3fn):
             raise TypeError(f"{n} must hold e4m3fn bytes (uint8 or float8_e4m3fn), got {t.dtype}")
-    T, Hq, Hkv, dqk, dv, out, lse = _varlen_common(q8, k8, v8, cu_seqlens, out, return_lse)
+    T, Tk, Hq, Hkv, dqk, dv, out, lse = _varlen_common(q8, k8, v8, cu_seqlens, out, return_lse, cu_seqlens_k)
     sm = 0.0 if softmax_scale is None else float(softmax_scale)
     _check(attn_fwd_fp8_varlen_raw(q8.data_ptr(), k8.data_ptr(), v8.data_ptr(), out.data_ptr(),
                                    0 if lse is None else lse.data_ptr(), cu_seqlens.data_ptr(),
-                                   cu_seqlens.numel() - 1, int(max_seqlen), T, float(q_scale), float(k_scale),
+                                   0 if cu_seqlens_k is None else cu_seqlens_k.data_ptr(),
+                                   cu_seqlens.numel() - 1, int(max_seqlen), T, Tk, float(q_scale), float(k_scale),
                                    float(v_scale), sm, Hq, Hkv, dqk, dv, int(bool(causal)), _P_MODES[p_mode],
                                    _stream_ptr(stream, q8.device)))
     return (out, lse) if return_lse else out
 
 
 def attn_fwd_bf16_varlen(q, k, v, cu_seqlens, max_seqlen, softmax_scale=None, causal=True, out=None, stream=None,
-                         return_lse=False):
+                         return_lse=False, cu_seqlens_k=None):
     """BF16 attention over a variable-length batch (layout as attn_fwd_fp8_varlen)."""
     for t, n in ((q, "q"), (k, "k"), (v, "v")):
         if t.dtype != torch.bfloat16:
             raise TypeError(f"{n} must be bfloat16, got {t.dtype}")
-    T, Hq, Hkv, dqk, dv, out, lse = _varlen_common(q, k, v, cu_seqlens, out, return_lse)
+    T, Tk, Hq, Hkv, dqk, dv, out, lse = _varlen_common(q, k, v, cu_seqlens, out, return_lse, cu_seqlens_k)
     sm = 0.0 if softmax_scale is None else float(softmax_scale)
     _check(attn_fwd_bf16_varlen_raw(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
                                     0 if lse is None else lse.data_ptr(), cu_seqlens.data_ptr(),
-                                    cu_seqlens.numel() - 1, int(max_seqlen), T, sm, Hq, Hkv, dqk, dv,
+                                    0 if cu_seqlens_k is None else cu_seqlens_k.data_ptr(),
+                                    cu_seqlens.numel() - 1, int(max_seqlen), T, Tk, sm, Hq, Hkv, dqk, dv,
                                     int(bool(causal)), _stream_ptr(stream, q.device)))
     return (out, lse) if return_lse else out

@@ -28,16 +28,17 @@ bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
     return a0 < b0 + nb && b0 < a0 + na;
 }
 
-// Shared checks; elem_qkv = bytes per Q/K/V element, rows = rows of the tensors
-// (B*S, or the packed total of a variable-length batch).  Returns ATTN_OK, an
-// error, or -1 for "empty problem, nothing to do".
 int finish(hipError_t e, const char* who);
 
+// Shared checks; elem_qkv = bytes per Q/K/V element, rows / rows_k = rows of Q,O /
+// K,V (B*S, or the packed totals of a variable-length batch).  Returns ATTN_OK, an
+// error, or -1 for "empty problem, nothing to do".
 int check_common(const void* q, const void* k, const void* v, void* o, const float* lse,
-                 float softmax_scale, int B, int Hq, int Hkv, int S, int64_t rows, int d_qk, int d_v,
-                 int causal, size_t elem_qkv, const char* who) {
+                 float softmax_scale, int B, int Hq, int Hkv, int S, int64_t rows, int64_t rows_k, int d_qk,
+                 int d_v, int causal, size_t elem_qkv, const char* who) {
     if (B < 0 || S < 0) return fail(ATTN_E_INVALID_ARG, "%s: B=%d and S=%d must be >= 0", who, B, S);
-    if (rows < 0) return fail(ATTN_E_INVALID_ARG, "%s: total rows %lld must be >= 0", who, (long long)rows);
+    if (rows < 0 || rows_k < 0)
+        return fail(ATTN_E_INVALID_ARG, "%s: total rows %lld / %lld must be >= 0", who, (long long)rows, (long long)rows_k);
     if (Hq <= 0 || Hkv <= 0) return fail(ATTN_E_INVALID_ARG, "%s: Hq=%d and Hkv=%d must be >= 1", who, Hq, Hkv);
     if (Hq % Hkv != 0) return fail(ATTN_E_INVALID_ARG, "%s: Hq=%d is not a multiple of Hkv=%d", who, Hq, Hkv);
     if (d_qk <= 0 || d_v <= 0) return fail(ATTN_E_INVALID_ARG, "%s: head dims d_qk=%d d_v=%d must be > 0", who, d_qk, d_v);
@@ -47,15 +48,15 @@ int check_common(const void* q, const void* k, const void* v, void* o, const flo
     if (d_v != 128) return fail(ATTN_E_UNSUPPORTED, "%s: d_v=%d unsupported (128)", who, d_v);
     // Every element offset is formed in 64-bit arithmetic by the kernels; the row
     // index and the head count must fit comfortably in 32-bit integers.
-    if (rows > (int64_t)1 << 30 || (int64_t)B * S > (int64_t)1 << 30)
-        return fail(ATTN_E_UNSUPPORTED, "%s: %lld rows too many", who, (long long)std::max<int64_t>(rows, (int64_t)B * S));
+    const int64_t most = std::max<int64_t>(std::max<int64_t>(rows, rows_k), (int64_t)B * S);
+    if (most > (int64_t)1 << 30) return fail(ATTN_E_UNSUPPORTED, "%s: %lld rows too many", who, (long long)most);
     if (B == 0 || S == 0 || rows == 0) return -1;
     if (!q || !k || !v || !o) return fail(ATTN_E_INVALID_ARG, "%s: null tensor pointer", who);
     if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o))
         return fail(ATTN_E_INVALID_ARG, "%s: tensor pointers must be 16-byte aligned", who);
     const size_t nq = (size_t)rows * Hq * d_qk * elem_qkv;
-    const size_t nk = (size_t)rows * Hkv * d_qk * elem_qkv;
-    const size_t nv = (size_t)rows * Hkv * d_v * elem_qkv;
+    const size_t nk = (size_t)rows_k * Hkv * d_qk * elem_qkv;
+    const size_t nv = (size_t)rows_k * Hkv * d_v * elem_qkv;
     const size_t no = (size_t)rows * Hq * d_v * 2;
     if (overlaps(o, no, q, nq) || overlaps(o, no, k, nk) || overlaps(o, no, v, nv))
         return fail(ATTN_E_INVALID_ARG, "%s: output overlaps an input", who);
@@ -79,10 +80,12 @@ int check_cu(const int* cu, int n_seqs, const char* who) {
 }
 
 int run_fp8(const void* q, const void* k, const void* v, void* o, float* lse, bool varlen, const int* cu, int total,
+            const int* cu_k, int total_k,
             float q_scale, float k_scale, float v_scale, float softmax_scale, int B, int Hq, int Hkv, int S,
             int d_qk, int d_v, int causal, int p_mode, hipStream_t stream, const char* who) {
     const int64_t rows = varlen ? (int64_t)total : (int64_t)B * S;
-    int st = check_common(q, k, v, o, lse, softmax_scale, B, Hq, Hkv, S, rows, d_qk, d_v, causal, 1, who);
+    const int64_t rows_k = varlen ? (int64_t)total_k : rows;
+    int st = check_common(q, k, v, o, lse, softmax_scale, B, Hq, Hkv, S, rows, rows_k, d_qk, d_v, causal, 1, who);
     if (st == -1) { g_err[0] = 0; return ATTN_OK; }
     if (st != ATTN_OK) return st;
     if (!(std::isfinite(q_scale) && q_scale > 0.f) || !(std::isfinite(k_scale) && k_scale > 0.f) ||
@@ -92,22 +95,24 @@ int run_fp8(const void* q, const void* k, const void* v, void* o, float* lse, bo
         return fail(ATTN_E_INVALID_ARG, "%s: p_mode=%d must be 0 (exact) or 1 (lean)", who, p_mode);
     attnfwd::Problem p{q, k, v, o, q_scale, k_scale, v_scale,
                        softmax_scale > 0.f ? softmax_scale : 1.0f / std::sqrt((float)d_qk),
-                       B, Hq, Hkv, S, d_qk, d_v, p_mode, stream, lse, causal, cu, (int)rows};
+                       B, Hq, Hkv, S, d_qk, d_v, p_mode, stream, lse, causal, cu, (int)rows, cu_k, (int)rows_k};
     const double c = (double)q_scale * k_scale * p.sm * 1.4426950408889634;
     if (!(c < 1e30 && c > 1e-30)) return fail(ATTN_E_INVALID_ARG, "%s: q_scale*k_scale*softmax_scale out of range", who);
     return finish(attnfwd::launch_fp8(p), who);
 }
 
 int run_bf16(const void* q, const void* k, const void* v, void* o, float* lse, bool varlen, const int* cu, int total,
+             const int* cu_k, int total_k,
              float softmax_scale, int B, int Hq, int Hkv, int S, int d_qk, int d_v, int causal,
              hipStream_t stream, const char* who) {
     const int64_t rows = varlen ? (int64_t)total : (int64_t)B * S;
-    int st = check_common(q, k, v, o, lse, softmax_scale, B, Hq, Hkv, S, rows, d_qk, d_v, causal, 2, who);
+    const int64_t rows_k = varlen ? (int64_t)total_k : rows;
+    int st = check_common(q, k, v, o, lse, softmax_scale, B, Hq, Hkv, S, rows, rows_k, d_qk, d_v, causal, 2, who);
     if (st == -1) { g_err[0] = 0; return ATTN_OK; }
     if (st != ATTN_OK) return st;
     attnfwd::Problem p{q, k, v, o, 1.f, 1.f, 1.f,
                        softmax_scale > 0.f ? softmax_scale : 1.0f / std::sqrt((float)d_qk),
-                       B, Hq, Hkv, S, d_qk, d_v, 0, stream, lse, causal, cu, (int)rows};
+                       B, Hq, Hkv, S, d_qk, d_v, 0, stream, lse, causal, cu, (int)rows, cu_k, (int)rows_k};
     return finish(attnfwd::launch_bf16(p), who);
 }
 
@@ -125,7 +130,7 @@ int attn_fwd_fp8_lse(const void* q, const void* k, const void* v, void* o, float
                      float q_scale, float k_scale, float v_scale, float softmax_scale,
                      int B, int Hq, int Hkv, int S, int d_qk, int d_v,
                      int causal, int p_mode, hipStream_t stream) {
-    return run_fp8(q, k, v, o, lse, false, nullptr, 0, q_scale, k_scale, v_scale, softmax_scale, B, Hq, Hkv, S, d_qk, d_v,
+    return run_fp8(q, k, v, o, lse, false, nullptr, 0, nullptr, 0, q_scale, k_scale, v_scale, softmax_scale, B, Hq, Hkv, S, d_qk, d_v,
                    causal, p_mode, stream, lse ? "attn_fwd_fp8_lse" : "attn_fwd_fp8");
 }
 
@@ -138,18 +143,21 @@ int attn_fwd_fp8(const void* q, const void* k, const void* v, void* o,
 }
 
 int attn_fwd_fp8_varlen(const void* q, const void* k, const void* v, void* o, float* lse,
-                        const int* cu_seqlens, int n_seqs, int max_seqlen, int total_tokens,
-                        float q_scale, float k_scale, float v_scale, float softmax_scale,
-                        int Hq, int Hkv, int d_qk, int d_v, int causal, int p_mode, hipStream_t stream) {
+                        const int* cu_seqlens_q, const int* cu_seqlens_k, int n_seqs, int max_seqlen_q,
+                        int total_q, int total_k, float q_scale, float k_scale, float v_scale,
+                        float softmax_scale, int Hq, int Hkv, int d_qk, int d_v, int causal, int p_mode,
+                        hipStream_t stream) {
     const char* who = "attn_fwd_fp8_varlen";
-    if (int st = check_cu(cu_seqlens, n_seqs, who)) return st;
-    return run_fp8(q, k, v, o, lse, true, cu_seqlens, total_tokens, q_scale, k_scale,
-                   v_scale, softmax_scale, n_seqs, Hq, Hkv, max_seqlen, d_qk, d_v, causal, p_mode, stream, who);
+    if (int st = check_cu(cu_seqlens_q, n_seqs, who)) return st;
+    if (int st = check_cu(cu_seqlens_k, 0, who)) return st;
+    const int* cu_k = cu_seqlens_k ? cu_seqlens_k : cu_seqlens_q;
+    return run_fp8(q, k, v, o, lse, true, cu_seqlens_q, total_q, cu_k, cu_seqlens_k ? total_k : total_q, q_scale, k_scale,
+                   v_scale, softmax_scale, n_seqs, Hq, Hkv, max_seqlen_q, d_qk, d_v, causal, p_mode, stream, who);
 }
 
 int attn_fwd_bf16_lse(const void* q, const void* k, const void* v, void* o, float* lse, float softmax_scale,
                       int B, int Hq, int Hkv, int S, int d_qk, int d_v, int causal, hipStream_t stream) {
-    return run_bf16(q, k, v, o, lse, false, nullptr, 0, softmax_scale, B, Hq, Hkv, S, d_qk, d_v, causal, stream,
+    return run_bf16(q, k, v, o, lse, false, nullptr, 0, nullptr, 0, softmax_scale, B, Hq, Hkv, S, d_qk, d_v, causal, stream,
                     lse ? "attn_fwd_bf16_lse" : "attn_fwd_bf16");
 }
 
@@ -159,12 +167,15 @@ int attn_fwd_bf16(const void* q, const void* k, const void* v, void* o, float so
 }
 
 int attn_fwd_bf16_varlen(const void* q, const void* k, const void* v, void* o, float* lse,
-                         const int* cu_seqlens, int n_seqs, int max_seqlen, int total_tokens,
-                         float softmax_scale, int Hq, int Hkv, int d_qk, int d_v, int causal, hipStream_t stream) {
+                         const int* cu_seqlens_q, const int* cu_seqlens_k, int n_seqs, int max_seqlen_q,
+                         int total_q, int total_k, float softmax_scale, int Hq, int Hkv, int d_qk, int d_v,
+                         int causal, hipStream_t stream) {
     const char* who = "attn_fwd_bf16_varlen";
-    if (int st = check_cu(cu_seqlens, n_seqs, who)) return st;
-    return run_bf16(q, k, v, o, lse, true, cu_seqlens, total_tokens, softmax_scale, n_seqs,
-                    Hq, Hkv, max_seqlen, d_qk, d_v, causal, stream, who);
+    if (int st = check_cu(cu_seqlens_q, n_seqs, who)) return st;
+    if (int st = check_cu(cu_seqlens_k, 0, who)) return st;
+    const int* cu_k = cu_seqlens_k ? cu_seqlens_k : cu_seqlens_q;
+    return run_bf16(q, k, v, o, lse, true, cu_seqlens_q, total_q, cu_k, cu_seqlens_k ? total_k : total_q,
+                    softmax_scale, n_seqs, Hq, Hkv, max_seqlen_q, d_qk, d_v, causal, stream, who);
 }
 
 int attn_rotate_quant_bf16(const void* x, void* x8, float* scale, int B, int S, int H, int d,
@@ -187,6 +198,6 @@ int attn_rotate_quant_bf16(const void* x, void* x8, float* scale, int B, int S, 
 
 const char* attn_last_error(void) { return g_err; }
 
-int attn_abi_version(void) { return 102; }
+int attn_abi_version(void) { return 103; }
 
 }  // extern "C"

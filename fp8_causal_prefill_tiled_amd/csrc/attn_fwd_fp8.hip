@@ -60,8 +60,10 @@ struct Fp8Params {
     float v_scale;
     int B, Hq, Hkv, S;
     int n_tiles;    // query tiles per head
-    const int* cu;  // variable-length batches: B + 1 token offsets (device), else null
-    int total;      // variable-length batches: rows of the packed tensors
+    const int* cu;    // variable-length batches: B + 1 query row offsets (device), else null
+    int total;        // variable-length batches: rows of the packed Q and O
+    const int* cu_k;  // variable-length batches: B + 1 key row offsets (device)
+    int total_k;      // variable-length batches: rows of the packed K and V
 };
 
 // 16-byte chunk swizzle of a V row in LDS.  The transposing read of one 16-lane
@@ -125,24 +127,34 @@ __global__ void __launch_bounds__(512) fp8_causal_fwd(Fp8Params a) {
     const int b = bh / a.Hq;
     const int h = bh - b * a.Hq;
     const int g = h / (a.Hq / a.Hkv);
-    // Sequence b: S rows starting at packed row tok0.  Equal-length batches are
-    // (B, S, H, d); a variable-length batch packs its sequences along the rows and
-    // a.S is the longest one.  The offsets are clamped into [0, total], so any
-    // contents of cu keep every access inside the tensors.
+    // Sequence b: S query rows from packed row tok0, Sk key rows from packed row
+    // tok0k; causal query i sees keys j <= i + qoff (qoff = Sk - S, the mask aligned
+    // at the bottom right).  Equal-length batches are (B, S, H, d) with Sk = S and
+    // qoff = 0; a variable-length batch packs its sequences along the rows, a.S
+    // being the longest query run.  The offsets are clamped into the tensors, so
+    // any contents of cu and cu_k keep every access inside them.
     int S = a.S;
+    int Sk = S;
+    int qoff = 0;
     int64_t tok0 = (int64_t)b * S;
+    int64_t tok0k = tok0;
     if constexpr (VARLEN) {
         const int t0 = min(max(a.cu[b], 0), a.total);
         const int t1 = min(max(a.cu[b + 1], t0), a.total);
+        const int u0 = min(max(a.cu_k[b], 0), a.total_k);
+        const int u1 = min(max(a.cu_k[b + 1], u0), a.total_k);
         S = min(t1 - t0, a.S);
+        Sk = u1 - u0;
+        qoff = Sk - S;
         tok0 = t0;
+        tok0k = u0;
         if (tile * BM >= S) return;   // whole workgroup: past the end of this sequence
     }
     const int q0 = tile * BM;
-    const int kend = CAUSAL ? min(S, q0 + BM) : S;
+    const int kend = !CAUSAL ? Sk : VARLEN ? max(min(Sk, q0 + BM + qoff), 0) : min(S, q0 + BM);
     const int nblk = (kend + KB - 1) / KB;        // key blocks the workgroup walks
     // first block that needs a mask: the diagonal one (causal) or the ragged last one
-    const int jdiag = CAUSAL ? q0 / KB : (S - 1) / KB;
+    const int jdiag = !CAUSAL ? (Sk - 1) / KB : VARLEN ? max(q0 + qoff, 0) / KB : q0 / KB;
 
     const int c = lane & 31;
     const int hh = lane >> 5;
@@ -151,8 +163,8 @@ __global__ void __launch_bounds__(512) fp8_causal_fwd(Fp8Params a) {
     const int64_t q_row = (int64_t)a.Hq * DQK;
     const int k_row = a.Hkv * DQK;                // bytes between consecutive keys
     const int v_row = a.Hkv * 128;
-    const uint8_t* kbase = a.k + tok0 * k_row + (int64_t)g * DQK;
-    const uint8_t* vbase = a.v + tok0 * v_row + (int64_t)g * 128;
+    const uint8_t* kbase = a.k + tok0k * k_row + (int64_t)g * DQK;
+    const uint8_t* vbase = a.v + tok0k * v_row + (int64_t)g * 128;
 
     // Q^T operands: lane (query c, half hh) holds d in [64kk + 32hh, +32) for each step kk.
     i32x8 qr[T::NKK];
@@ -190,7 +202,7 @@ __global__ void __launch_bounds__(512) fp8_causal_fwd(Fp8Params a) {
     auto gload = [&](int j) {
         // rows of block j inside the tensor, clamped to [0, KB]; uniform, so kept on the
         // scalar unit (a fused vector med3 would cost three vector instructions per block)
-        const int rows = min(__builtin_amdgcn_readfirstlane(max(S - j * KB, 0)), KB);
+        const int rows = min(__builtin_amdgcn_readfirstlane(max(Sk - j * KB, 0)), KB);
         if (grp == 0) {
             const auto r = buffer_rsrc(kbase + (int64_t)j * KB * k_row, rows * k_row);
 #pragma unroll
@@ -299,7 +311,7 @@ __global__ void __launch_bounds__(512) fp8_causal_fwd(Fp8Params a) {
         if (j >= jdiag) {
             // key kb0 + off(r) + 4hh is visible iff off(r) <= qlim - kb0 - 4hh, qlim the
             // last key the query sees
-            const int qlim = CAUSAL ? min(qabs, S - 1) : S - 1;
+            const int qlim = CAUSAL ? min(qabs + qoff, Sk - 1) : Sk - 1;
             const int lim = qlim - j * KB - 4 * hh;
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
@@ -480,6 +492,9 @@ __global__ void __launch_bounds__(512) fp8_causal_fwd(Fp8Params a) {
     // d = 32dt + 8(r/4) + 4hh + r%4.  L = sum_j 2^(t_j - ref) over the rounded
     // probabilities, so the row's natural-log normaliser is ln2 * (log2 L + ref).
     const float l0 = lsum[0];
+    // a query of a variable-length sequence that sees no key (more queries than keys)
+    // has L = 0 and O = 0: divide by infinity instead, so its output is 0
+    const float l0d = (VARLEN && !(l0 > 0.0f)) ? INFINITY : l0;
     if (LSE && hh == 0 && qabs < S)
         a.lse[(VARLEN ? (int64_t)h * a.total + tok0 : ((int64_t)b * a.Hq + h) * S) + qabs] = (log2f(l0) + ref) * 0.6931471805599453f;
     if (qabs < S) {
@@ -488,10 +503,10 @@ __global__ void __launch_bounds__(512) fp8_causal_fwd(Fp8Params a) {
         for (int dt = 0; dt < 4; ++dt) {
 #pragma unroll
             for (int r4 = 0; r4 < 4; ++r4) {
-                float x0 = (o[dt][4 * r4 + 0] / l0) * a.v_scale;
-                float x1 = (o[dt][4 * r4 + 1] / l0) * a.v_scale;
-                float x2 = (o[dt][4 * r4 + 2] / l0) * a.v_scale;
-                float x3 = (o[dt][4 * r4 + 3] / l0) * a.v_scale;
+                float x0 = (o[dt][4 * r4 + 0] / l0d) * a.v_scale;
+                float x1 = (o[dt][4 * r4 + 1] / l0d) * a.v_scale;
+                float x2 = (o[dt][4 * r4 + 2] / l0d) * a.v_scale;
+                float x3 = (o[dt][4 * r4 + 3] / l0d) * a.v_scale;
                 uint2 pk = make_uint2(pack_bf16x2(x0, x1), pack_bf16x2(x2, x3));
                 *reinterpret_cast<uint2*>(op + 32 * dt + 8 * r4 + 4 * hh) = pk;
             }
@@ -519,6 +534,8 @@ hipError_t launch_t(const Problem& p) {
     a.S = p.S;
     a.cu = p.cu;
     a.total = p.total;
+    a.cu_k = p.cu_k;
+    a.total_k = p.total_k;
     a.n_tiles = (p.S + BM - 1) / BM;
     const long long nblocks = (long long)a.n_tiles * p.B * p.Hq;
     if (nblocks <= 0 || nblocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;

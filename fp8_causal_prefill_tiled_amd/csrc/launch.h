@@ -18,11 +18,15 @@ struct Problem {
     hipStream_t stream;
     float* lse;   // (B, Hq, S) fp32 per-row log-sum-exp output, or null
     int causal;   // 1: key j visible to query i iff j <= i; 0: every key visible
-    // Variable-length batch: B sequences packed along the rows, sequence b at rows
-    // cu[b]..cu[b+1]-1 (device pointer, B + 1 entries), S = the longest, total = rows
-    // of the packed tensors.  cu == nullptr: equal-length (B, S, H, d) tensors.
+    // Variable-length batch: B sequences packed along the rows, sequence b's queries at
+    // rows cu[b]..cu[b+1]-1 of Q and O and its keys at rows cu_k[b]..cu_k[b+1]-1 of K
+    // and V (device pointers, B + 1 entries each); S = the longest query run, total and
+    // total_k = rows of the packed Q/O and K/V.  cu == nullptr: equal-length
+    // (B, S, H, d) tensors.
     const int* cu;
     int total;
+    const int* cu_k;
+    int total_k;
 };
 
 hipError_t launch_fp8(const Problem& p);

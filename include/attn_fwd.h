@@ -166,37 +166,44 @@ int attn_rotate_quant_bf16(const void* x, void* x8, float* scale, int B, int S, 
                            hipStream_t stream);
 
 /*
- * Variable-length batches: n_seqs sequences of different lengths packed along
- * the rows (the flash_attn_varlen_func convention), each attending only to
- * itself (causal within the sequence when causal == 1).  The pages list
- * variable batch sizing among what their kernels do not yet cover ("Breaking
- * the FP8 Attention Bottleneck on AMD MI355X", section "Application Boundaries
- * and Engineering Decisions"); this is the same kernel with per-sequence row
- * offsets.
+ * Variable-length batches: n_seqs sequences packed along the rows (the
+ * flash_attn_varlen_func convention), each attending only to itself.  The
+ * pages list variable batch sizing among what their kernels do not yet cover
+ * ("Breaking the FP8 Attention Bottleneck on AMD MI355X", section
+ * "Application Boundaries and Engineering Decisions"); this is the same kernel
+ * with per-sequence row offsets.  A sequence may have fewer queries than keys
+ * (a chunk of queries after a cached key prefix) or more: with Sq queries and
+ * Sk keys the causal mask is aligned at the bottom right, query i seeing keys
+ * j <= i + Sk - Sq (FlashAttention's convention; equal lengths give the usual
+ * mask).  A query that sees no key gets O = 0 and lse = -inf.
  *
- * q: (total_tokens, Hq, d_qk), k: (total_tokens, Hkv, d_qk), v: (total_tokens,
- *    Hkv, d_v), o: (total_tokens, Hq, d_v) bf16, contiguous, 16-byte aligned.
- * cu_seqlens: device pointer to n_seqs + 1 int32 row offsets, 4-byte aligned:
- *    sequence i is rows cu_seqlens[i] .. cu_seqlens[i+1]-1.  Expected:
- *    cu_seqlens[0] = 0, non-decreasing, cu_seqlens[n_seqs] <= total_tokens,
- *    every length <= max_seqlen.  The contents are not read on the host (no
- *    synchronisation); the kernels clamp every offset into [0, total_tokens] and
- *    every length to max_seqlen, so any contents keep all accesses in bounds.
- *    Rows outside every sequence are left unwritten.
- * lse: NULL, or Hq * total_tokens floats, layout (Hq, total_tokens).
- * The grid covers ceil(max_seqlen / 256) query tiles per (sequence, head);
+ * q: (total_q, Hq, d_qk), o: (total_q, Hq, d_v) bf16, k: (total_k, Hkv, d_qk),
+ *    v: (total_k, Hkv, d_v); contiguous, 16-byte aligned.
+ * cu_seqlens_q: device pointer to n_seqs + 1 int32 row offsets, 4-byte aligned:
+ *    sequence i's queries are rows cu_seqlens_q[i] .. cu_seqlens_q[i+1]-1 of q/o.
+ * cu_seqlens_k: the same for k/v, or NULL: keys at the query offsets
+ *    (total_k is then ignored and taken equal to total_q).
+ * Expected: offsets start at 0, never decrease, end at most at the totals,
+ *    every query run at most max_seqlen_q.  The contents are not read on the host
+ *    (no synchronisation); the kernels clamp every offset into its tensor and
+ *    every query run to max_seqlen_q, so any contents keep all accesses in
+ *    bounds.  Rows outside every sequence are left unwritten.
+ * lse: NULL, or Hq * total_q floats, layout (Hq, total_q).
+ * The grid covers ceil(max_seqlen_q / 256) query tiles per (sequence, head);
  * tiles past a sequence's end exit at once.  Other arguments, behaviour and
- * errors as attn_fwd_fp8_lse / attn_fwd_bf16_lse; n_seqs == 0, max_seqlen == 0
- * or total_tokens == 0 is an empty problem (ATTN_OK, nothing launched).
+ * errors as attn_fwd_fp8_lse / attn_fwd_bf16_lse; n_seqs == 0,
+ * max_seqlen_q == 0 or total_q == 0 is an empty problem (ATTN_OK, nothing
+ * launched).
  */
 int attn_fwd_fp8_varlen(const void* q, const void* k, const void* v, void* o, float* lse,
-                        const int* cu_seqlens, int n_seqs, int max_seqlen, int total_tokens,
-                        float q_scale, float k_scale, float v_scale, float softmax_scale,
-                        int Hq, int Hkv, int d_qk, int d_v, int causal, int p_mode, hipStream_t stream);
+                        const int* cu_seqlens_q, const int* cu_seqlens_k, int n_seqs, int max_seqlen_q,
+                        int total_q, int total_k, float q_scale, float k_scale, float v_scale,
+                        float softmax_scale, int Hq, int Hkv, int d_qk, int d_v, int causal, int p_mode,
+                        hipStream_t stream);
 int attn_fwd_bf16_varlen(const void* q, const void* k, const void* v, void* o, float* lse,
-                         const int* cu_seqlens, int n_seqs, int max_seqlen, int total_tokens,
-                         float softmax_scale, int Hq, int Hkv, int d_qk, int d_v, int causal,
-                         hipStream_t stream);
+                         const int* cu_seqlens_q, const int* cu_seqlens_k, int n_seqs, int max_seqlen_q,
+                         int total_q, int total_k, float softmax_scale, int Hq, int Hkv, int d_qk, int d_v,
+                         int causal, hipStream_t stream);
 
 /* Message for the calling thread's last non-OK status ("" if none).  The
  * returned storage is thread-local and valid until that thread's next call. */

@@ -36,7 +36,7 @@ def test_exports_every_declared_symbol(lib):
     assert {"attn_fwd_fp8", "attn_fwd_fp8_lse", "attn_fwd_fp8_varlen", "attn_fwd_bf16", "attn_fwd_bf16_lse",
             "attn_fwd_bf16_varlen", "attn_last_error", "attn_abi_version"} <= decl
     assert decl <= binding.exported_symbols()
-    assert lib.attn_abi_version() == 102
+    assert lib.attn_abi_version() == 103
 
 
 # fake, never-dereferenced, 16-byte aligned device addresses of disjoint buffers
@@ -128,24 +128,33 @@ def test_lse_host_validation(lib, entry, kw, status):
 
 
 CU = 0x60000000
+OK_IF_NULL_K = "ok-if-null-k"
 
 
 @pytest.mark.parametrize("entry", ["fp8", "bf16"])
 @pytest.mark.parametrize("kw,status", [
-    (dict(cu_seqlens=0), INVALID),                          # null offsets with sequences
-    (dict(cu_seqlens=CU + 2), INVALID),                     # misaligned offsets
-    (dict(total_tokens=-1), INVALID), (dict(max_seqlen=-1), INVALID), (dict(n_seqs=-1), INVALID),
-    (dict(total_tokens=(1 << 30) + 1), UNSUPPORTED),
+    (dict(cu_seqlens_q=0), INVALID),                        # null offsets with sequences
+    (dict(cu_seqlens_q=CU + 2), INVALID),                   # misaligned offsets
+    (dict(cu_seqlens_k=CU + 6), INVALID),
+    (dict(total_q=-1), INVALID), (dict(total_k=-1), INVALID), (dict(max_seqlen_q=-1), INVALID),
+    (dict(n_seqs=-1), INVALID),
+    (dict(total_q=(1 << 30) + 1), UNSUPPORTED), (dict(total_k=(1 << 30) + 1), UNSUPPORTED),
+    (dict(cu_seqlens_k=0, total_k=-5), OK_IF_NULL_K),       # null key offsets: total_k ignored
+    (dict(k=O + 4096), INVALID),                            # K starting inside O
     (dict(d_qk=64), UNSUPPORTED), (dict(Hq=3), INVALID), (dict(causal=2), INVALID),
     (dict(lse=Q + 64), INVALID),                            # lse inside Q
     (dict(o=Q + 4096), INVALID),                            # output overlaps Q
-    (dict(n_seqs=0, cu_seqlens=0, q=0, k=0, v=0, o=0), OK),  # empty: nothing launched
-    (dict(total_tokens=0, q=0, k=0, v=0, o=0), OK),
-    (dict(max_seqlen=0, q=0, k=0, v=0, o=0), OK),
+    (dict(n_seqs=0, cu_seqlens_q=0, cu_seqlens_k=0, q=0, k=0, v=0, o=0), OK),  # empty: nothing launched
+    (dict(total_q=0, q=0, k=0, v=0, o=0), OK),
+    (dict(max_seqlen_q=0, q=0, k=0, v=0, o=0), OK),
 ])
 def test_varlen_host_validation(lib, entry, kw, status):
-    a = dict(q=Q, k=K, v=V, o=O, lse=LSE, cu_seqlens=CU, n_seqs=3, max_seqlen=100, total_tokens=200,
-             softmax_scale=0.0, Hq=4, Hkv=2, d_qk=128, d_v=128, causal=1)
+    if status == OK_IF_NULL_K:
+        # a null cu_seqlens_k with a garbage total_k is accepted; check it on an empty problem
+        kw = dict(kw, n_seqs=0, cu_seqlens_q=0, q=0, k=0, v=0, o=0)
+        status = OK
+    a = dict(q=Q, k=K, v=V, o=O, lse=LSE, cu_seqlens_q=CU, cu_seqlens_k=CU + 64, n_seqs=3, max_seqlen_q=100,
+             total_q=200, total_k=300, softmax_scale=0.0, Hq=4, Hkv=2, d_qk=128, d_v=128, causal=1)
     if entry == "fp8":
         a.update(q_scale=1.0, k_scale=1.0, v_scale=1.0, p_mode=1)
     a.update(kw)

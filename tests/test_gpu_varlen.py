@@ -124,3 +124,94 @@ def test_rows_outside_sequences_untouched_and_offsets_clamped(entry):
     torch.cuda.synchronize()
     assert torch.equal(out[120:], sentinel[120:])
     assert bool(torch.isfinite(out[:120].float()).all()) and bool(torch.isfinite(lse[:, :120]).all())
+
+
+# ------------------------------------------------- unequal query and key lengths
+
+PAIRS = [(64, 300), (1, 257), (200, 200), (130, 1000), (256, 513)]   # (Sq, Sk), Sq <= Sk
+
+
+def _cu_from(lens):
+    return _cu(list(lens))
+
+
+@pytest.mark.parametrize("causal", [True, False])
+@pytest.mark.parametrize("mode", ["lean", "exact"])
+@pytest.mark.parametrize("dqk", [128, 192])
+def test_fp8_fewer_queries_than_keys_is_the_tail_of_the_full_call(dqk, mode, causal):
+    # A sequence with Sq queries over Sk >= Sq keys (bottom-right aligned) is, row for row, the
+    # last Sq rows of the equal-length call whose queries end with these: same key blocks, same
+    # masks, same order, so the bytes must match.
+    Sks = [sk for _, sk in PAIRS]
+    qf8, k8, v8, qs, ks, vs = _packed_fp8(Sks, 4, 2, dqk, 1300)
+    qf8, k8, v8 = qf8.to(DEV), k8.to(DEV), v8.to(DEV)
+    offs = np.concatenate([[0], np.cumsum(Sks)])
+    q8 = torch.cat([qf8[offs[i] + sk - sq:offs[i] + sk] for i, (sq, sk) in enumerate(PAIRS)])
+    out, lse = binding.attn_fwd_fp8_varlen(q8, k8, v8, _cu_from(sq for sq, _ in PAIRS), max(sq for sq, _ in PAIRS),
+                                           qs, ks, vs, p_mode=mode, causal=causal, return_lse=True,
+                                           cu_seqlens_k=_cu_from(Sks))
+    torch.cuda.synchronize()
+    qo = 0
+    for i, (sq, sk) in enumerate(PAIRS):
+        sl = slice(offs[i], offs[i] + sk)
+        of, lf = binding.attn_fwd_fp8(qf8[None, sl].contiguous(), k8[None, sl].contiguous(), v8[None, sl].contiguous(),
+                                      qs, ks, vs, p_mode=mode, causal=causal, return_lse=True)
+        torch.cuda.synchronize()
+        assert torch.equal(out[qo:qo + sq].view(torch.int16), of[0, sk - sq:].view(torch.int16)), (sq, sk)
+        assert torch.equal(lse[:, qo:qo + sq], lf[0, :, sk - sq:]), (sq, sk)
+        qo += sq
+
+
+@pytest.mark.parametrize("mode", ["lean", "exact"])
+def test_fp8_unequal_lengths_against_oracle(mode):
+    # includes more queries than keys: the first Sq - Sk queries see nothing (O = 0, lse = -inf)
+    pairs = [(100, 300), (300, 100), (65, 64), (1, 1), (40, 0)]
+    g = torch.Generator().manual_seed(77)
+    qf = torch.randn((sum(p[0] for p in pairs), 2, 128), generator=g)
+    kf = torch.randn((sum(p[1] for p in pairs), 1, 128), generator=g)
+    vf = torch.randn((sum(p[1] for p in pairs), 1, 128), generator=g)
+    (q8, qs), (k8, ks), (v8, vs) = (W.quantize_e4m3(x) for x in (qf, kf, vf))
+    cq, ck = _cu_from(p[0] for p in pairs), _cu_from(p[1] for p in pairs)
+    out, lse = binding.attn_fwd_fp8_varlen(q8.to(DEV), k8.to(DEV), v8.to(DEV), cq, max(p[0] for p in pairs),
+                                           qs, ks, vs, p_mode=mode, return_lse=True, cu_seqlens_k=ck)
+    torch.cuda.synchronize()
+    got = out.float().cpu().numpy().astype(np.float64)
+    gl = lse.cpu().numpy().astype(np.float64)
+    emus, refs, lemus, qo, ko = [], [], [], 0, 0
+    for sq, sk in pairs:
+        d = {"q8": q8[None, qo:qo + sq], "k8": k8[None, ko:ko + sk], "v8": v8[None, ko:ko + sk],
+             "q_scale": qs, "k_scale": ks, "v_scale": vs}
+        emu, ref, lemu, lref = oracle_fp8(d, mode, with_lse=True)
+        emus.append(emu)
+        refs.append(ref)
+        lemus.append(lemu)
+        blind = max(sq - sk, 0)                  # queries that see no key
+        assert np.all(got[qo:qo + blind] == 0) and np.all(np.isneginf(gl[:, qo:qo + blind]))
+        fin = np.isfinite(lemu[0])
+        assert np.array_equal(np.isfinite(gl[:, qo:qo + sq]), fin)
+        if fin.any():
+            assert np.max(np.abs(gl[:, qo:qo + sq][fin] - lemu[0][fin])) < np.log(1.125)
+        qo += sq
+        ko += sk
+    check_fp8(got[None], np.concatenate(emus, axis=1), np.concatenate(refs, axis=1), f"unequal {pairs} {mode}")
+
+
+def test_bf16_fewer_queries_than_keys_is_the_tail_of_the_full_call():
+    Sks = [sk for _, sk in PAIRS]
+    qf, kf, vf = (x.to(torch.bfloat16).to(DEV) for x in _draws(Sks, 4, 2, 128, 41))
+    offs = np.concatenate([[0], np.cumsum(Sks)])
+    q = torch.cat([qf[offs[i] + sk - sq:offs[i] + sk] for i, (sq, sk) in enumerate(PAIRS)])
+    for causal in (True, False):
+        out, lse = binding.attn_fwd_bf16_varlen(q, kf, vf, _cu_from(sq for sq, _ in PAIRS),
+                                                max(sq for sq, _ in PAIRS), causal=causal, return_lse=True,
+                                                cu_seqlens_k=_cu_from(Sks))
+        torch.cuda.synchronize()
+        qo = 0
+        for i, (sq, sk) in enumerate(PAIRS):
+            sl = slice(offs[i], offs[i] + sk)
+            of, lf = binding.attn_fwd_bf16(qf[None, sl].contiguous(), kf[None, sl].contiguous(),
+                                           vf[None, sl].contiguous(), causal=causal, return_lse=True)
+            torch.cuda.synchronize()
+            assert torch.equal(out[qo:qo + sq].view(torch.int16), of[0, sk - sq:].view(torch.int16)), (sq, sk)
+            assert torch.equal(lse[:, qo:qo + sq], lf[0, :, sk - sq:]), (sq, sk)
+            qo += sq
