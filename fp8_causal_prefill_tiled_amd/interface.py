@@ -112,3 +112,37 @@ def flash_attn_func(q, k, v, dropout_p=0.0, softmax_scale=None, causal=False, wi
     if return_attn_probs:
         return out, lse, None
     return out
+
+
+def flash_attn_varlen_func(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k=None, dropout_p=0.0,
+                           softmax_scale=None, causal=False, window_size=(-1, -1), softcap=0.0, alibi_slopes=None,
+                           deterministic=False, return_attn_probs=False, *, q_descale=None, k_descale=None,
+                           v_descale=None, p_mode="lean"):
+    """Variable-length forward attention in the ``flash_attn_varlen_func`` calling convention.
+
+    q: (total_q, Hq, d_qk), k/v: (total_k, Hkv, d), sequences packed along the rows at the int32
+    GPU offsets ``cu_seqlens_q`` / ``cu_seqlens_k``; a sequence with fewer (or more) queries than
+    keys uses the bottom-right aligned causal mask.  ``max_seqlen_q`` is the longest query run
+    (``max_seqlen_k`` is accepted for the signature and not needed).  bfloat16 or e4m3 inputs as
+    for flash_attn_func.  Returns O (total_q, Hq, d_v), or (O, lse (Hq, total_q), None).
+    """
+    if dropout_p != 0.0 or tuple(window_size) != (-1, -1) or softcap != 0.0 or alibi_slopes is not None:
+        raise NotImplementedError("dropout, sliding windows, softcapping and ALiBi are not supported")
+    if q.dtype in _FP8_DTYPES:
+        if k.dtype not in _FP8_DTYPES or v.dtype not in _FP8_DTYPES:
+            raise TypeError("q, k and v must all be FP8 e4m3 (or all bfloat16)")
+        q8, k8, v8 = (t.view(torch.uint8) if t.dtype != torch.uint8 else t for t in (q, k, v))
+        res = binding.attn_fwd_fp8_varlen(q8, k8, v8, cu_seqlens_q, max_seqlen_q, _scale(q_descale, "q_descale"),
+                                          _scale(k_descale, "k_descale"), _scale(v_descale, "v_descale"),
+                                          softmax_scale=softmax_scale, causal=causal, p_mode=p_mode,
+                                          return_lse=return_attn_probs, cu_seqlens_k=cu_seqlens_k)
+    elif q.dtype == torch.bfloat16:
+        if k.dtype != torch.bfloat16 or v.dtype != torch.bfloat16:
+            raise TypeError("q, k and v must all be bfloat16 (or all FP8 e4m3)")
+        res = binding.attn_fwd_bf16_varlen(q, k, v, cu_seqlens_q, max_seqlen_q, softmax_scale=softmax_scale,
+                                           causal=causal, return_lse=return_attn_probs, cu_seqlens_k=cu_seqlens_k)
+    else:
+        raise TypeError(f"unsupported input dtype {q.dtype}: bfloat16 or float8_e4m3fn")
+    if return_attn_probs:
+        return res[0], res[1], None
+    return res

@@ -71,3 +71,26 @@ def test_opcheck():
     b = W.make_bf16(W.Workload("iface", 1, 4, 2, 130, 128, 128), seed=4)
     q, k, v = (b[n].to(DEV) for n in ("q", "k", "v"))
     torch.library.opcheck(_attn_fwd_bf16_op, (q, k, v, 0.0, False, True))
+
+
+def test_varlen_wrapper_matches_binding():
+    from fp8_causal_prefill_tiled_amd.interface import flash_attn_varlen_func
+    g = torch.Generator().manual_seed(5)
+    q = torch.randn((150, 4, 128), generator=g).to(torch.bfloat16).to(DEV)
+    k = torch.randn((400, 2, 128), generator=g).to(torch.bfloat16).to(DEV)
+    v = torch.randn((400, 2, 128), generator=g).to(torch.bfloat16).to(DEV)
+    cq = torch.tensor([0, 50, 150], dtype=torch.int32, device=DEV)
+    ck = torch.tensor([0, 300, 400], dtype=torch.int32, device=DEV)
+    ref, ref_lse = binding.attn_fwd_bf16_varlen(q, k, v, cq, 100, causal=True, return_lse=True, cu_seqlens_k=ck)
+    out, lse, _ = flash_attn_varlen_func(q, k, v, cq, ck, 100, 300, causal=True, return_attn_probs=True)
+    q8, qs = W.quantize_e4m3(q.float().cpu())
+    k8, ks = W.quantize_e4m3(k.float().cpu())
+    v8, vs = W.quantize_e4m3(v.float().cpu())
+    q8, k8, v8 = q8.to(DEV), k8.to(DEV), v8.to(DEV)
+    ref8 = binding.attn_fwd_fp8_varlen(q8, k8, v8, cq, 100, qs, ks, vs, p_mode="lean", cu_seqlens_k=ck)
+    out8 = flash_attn_varlen_func(q8.view(torch.float8_e4m3fn), k8.view(torch.float8_e4m3fn),
+                                  v8.view(torch.float8_e4m3fn), cq, ck, 100, causal=True,
+                                  q_descale=qs, k_descale=ks, v_descale=vs)
+    torch.cuda.synchronize()
+    assert torch.equal(out.view(torch.int16), ref.view(torch.int16)) and torch.equal(lse, ref_lse)
+    assert torch.equal(out8.view(torch.int16), ref8.view(torch.int16))
