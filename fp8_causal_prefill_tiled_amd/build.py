@@ -43,9 +43,10 @@ def kernel_flags(src):
     # isfinite() tests must see NaN): inputs are finite by contract, so fmaxf
     # lowers to bare v_max3_f32 without NaN quieting.
     flags = ["-fno-honor-nans"] if src.endswith(".hip") else []
-    if src in ("attn_fwd_fp8.hip", "attn_fwd_bf16.hip"):
+    if src in ("attn_fwd_fp8.hip", "attn_fwd_bf16.hip", "rotate_quant.hip"):
         # all matrix results in VGPRs: the score MFMAs' are read directly by the
-        # probability code, and the P.V accumulators' inline-asm MFMA ties them there
+        # probability code, the P.V accumulators' inline-asm MFMA ties them there, and
+        # the rotation's products feed vector butterflies
         flags += ["-mllvm", "-amdgpu-mfma-vgpr-form"]
     return flags
 

@@ -10,16 +10,25 @@
 // for an all-zero tensor.  H is orthogonal, so the attention scores of rotated
 // Q and K equal the originals: the rotated codes go straight into attn_fwd_fp8.
 //
-// Layout: rows are contiguous and d is a multiple of n, so the tensor is a
-// sequence of n-element blocks.  LB = n/8 consecutive lanes hold one block, 8
-// bf16 per lane (one 16-byte load); the fast Walsh-Hadamard transform runs its 3
-// low butterfly stages inside the lane and log2(LB) stages across lanes (lane-xor
-// moves within the block's aligned lane group, by DPP).  Four stream-ordered launches:
-// zero the amax cell; rotate and reduce max|y| (per workgroup, then an atomic max
-// on the float's bits, order-preserving for non-negative floats, skipped when
-// the cell already holds more); rotate again and quantise with the final scale; turn
-// the cell into the scale.  The work is HBM streaming: each of the two passes
-// reads the bf16 tensor once, the second writes one byte per element.
+// Rotation on the matrix cores.  Rows are contiguous and d is a multiple of n, so
+// the tensor is a sequence of n-element blocks, n = 32 NA.  The Sylvester matrix
+// factors as H_n = H_NA (x) H_32, so for a block split into NA chunks x_a of 32,
+//     z_a = x_a H_32                   (matrix cores: exact bf16 inputs, fp32 sums)
+//     y_b = sum_a H_NA[a][b] z_a       (an NA-point butterfly inside the lane, fp32)
+// is y = x H_n.  A wave takes 32 consecutive blocks and computes the product
+// transposed, Z_a^T = H_32 . X_a^T, with two v_mfma_f32_32x32x16_bf16 per chunk:
+// the A operand is H_32 (constant +-1 in registers), the B operand the blocks, so
+// each lane loads 16 contiguous bytes of one block per operand and ends holding,
+// for block l%32, the rotated columns 8(r/4) + 4(l/32) + r%4 of every chunk: four
+// consecutive columns per group of four accumulators, one 32-bit store of e4m3
+// codes.  The vector work left is NA log2(NA) adds per 32 elements plus the
+// maximum or the quantisation, so both passes stream at HBM rate.
+//
+// Four stream-ordered launches: zero the amax cell; rotate and reduce max|y| (per
+// workgroup, then an atomic max on the float's bits, order-preserving for
+// non-negative floats, skipped when the cell already holds more); rotate again
+// and quantise with the final scale; turn the cell into the scale.  Each of the
+// two passes reads the bf16 tensor once, the second writes one byte per element.
 #include "common.h"
 #include "launch.h"
 
@@ -28,80 +37,87 @@ namespace {
 
 constexpr float kE4M3Max = 448.0f;
 constexpr int kThreads = 256;
+constexpr int U = 2;   // 32-block units per wave and loop step (loads in flight)
 
-// Value of lane i ^ M (M = 1, 2, 4, 8) by data-parallel-primitive moves, no LDS:
-// quad permutations give xor 1, 2 and 3; the half-row mirror is xor 7 and the row
-// mirror xor 15 within 16 lanes, so xor 4 = (xor 7 then xor 3) and xor 8 = (xor 15
-// then xor 7).
-template <int M>
-__device__ __forceinline__ float xor_lane(float v) {
-    constexpr int kQuadXor1 = 0xB1, kQuadXor2 = 0x4E, kQuadXor3 = 0x1B, kRowMirror = 0x140, kRowHalfMirror = 0x141;
-    int x = __float_as_int(v);
-    if constexpr (M == 1) {
-        x = __builtin_amdgcn_update_dpp(0, x, kQuadXor1, 0xF, 0xF, false);
-    } else if constexpr (M == 2) {
-        x = __builtin_amdgcn_update_dpp(0, x, kQuadXor2, 0xF, 0xF, false);
-    } else if constexpr (M == 4) {
-        x = __builtin_amdgcn_update_dpp(0, x, kRowHalfMirror, 0xF, 0xF, false);
-        x = __builtin_amdgcn_update_dpp(0, x, kQuadXor3, 0xF, 0xF, false);
-    } else {
-        static_assert(M == 8, "xor within 16 lanes");
-        x = __builtin_amdgcn_update_dpp(0, x, kRowMirror, 0xF, 0xF, false);
-        x = __builtin_amdgcn_update_dpp(0, x, kRowHalfMirror, 0xF, 0xF, false);
-    }
-    return __int_as_float(x);
+// Rows of the H_32 A operand held by this lane for K half kk: element i is
+// H_32[l % 32][16 kk + 8 (l / 32) + i] = (-1)^popcount(row & col), as bf16.
+__device__ __forceinline__ bf16x8 h32_operand(int lane, int kk) {
+    const int row = lane & 31, col0 = 16 * kk + 8 * (lane >> 5);
+    i16x8 bits;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) bits[i] = (__builtin_popcount(row & (col0 + i)) & 1) ? (short)0xBF80 : (short)0x3F80;
+    return __builtin_bit_cast(bf16x8, bits);
 }
 
-// One cross-lane butterfly stage over the U blocks a lane holds: partner lane
-// t ^ M (lower index a + b, upper a - b).
-template <int M, int NU>
-__device__ __forceinline__ void cross_stage(float (&x)[NU][8], int t) {
-    const bool upper = (t & M) != 0;
+// Bytes of one bf16 block row in the LDS staging tile: padded by 16 so that the
+// 16-byte operand reads of 32 rows fall on spread banks and stay aligned.
+template <int NA>
+constexpr int kInRow = 64 * NA + 16;
+
+// Global -> registers -> LDS for U units of 32 blocks (each unit 64 NA bytes per
+// block, contiguous): every load instruction reads 1 KiB of consecutive bytes.
+// Blocks at or past nblocks read as zeros.
+template <int NA>
+__device__ __forceinline__ void stage_in(const __bf16* __restrict__ x, int64_t unit0, int64_t nblocks, int lane,
+                                         ATTN_LDS uint8_t* tile) {
+    constexpr int NB = 32 * NA, CPB = NB * 2 / 16;           // 16-byte chunks per block
+    constexpr int IT = 32 * CPB / 64;                         // chunks per lane and unit
+    i32x4 v[U][IT];
 #pragma unroll
-    for (int u = 0; u < NU; ++u)
+    for (int u = 0; u < U; ++u)
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const float p = xor_lane<M>(x[u][i]);
-            x[u][i] = upper ? p - x[u][i] : x[u][i] + p;
+        for (int it = 0; it < IT; ++it) {
+            const int k = it * 64 + lane, c = k / CPB;
+            const int64_t blk = (unit0 + u) * 32 + c;
+            v[u][it] = blk < nblocks ? load16(x + blk * NB + 8 * (k % CPB)) : i32x4{0, 0, 0, 0};
+        }
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+#pragma unroll
+        for (int it = 0; it < IT; ++it) {
+            const int k = it * 64 + lane;
+            lds_store16(tile + (u * 32 + k / CPB) * kInRow<NA> + 16 * (k % CPB), v[u][it]);
         }
 }
 
-// Unnormalised transform of NU blocks at once (each stage runs over all of them
-// before the next, so consecutive dependent lane moves are far apart), y_i =
-// sum_j (-1)^popcount(i & j) x_j: bit b of the element index is one butterfly
-// stage (lower index a + b, upper a - b).  Lane t of a block holds elements
-// 8t .. 8t+7.
-template <int LB, int NU>
-__device__ __forceinline__ void fwht(float (&x)[NU][8], int t) {
+// The NA-chunk rotation of one staged unit of 32 blocks, transposed: y[b][r] is
+// column 32 b + 8 (r/4) + 4 (lane/32) + r%4 of block lane % 32 (unnormalised).
+template <int NA>
+__device__ __forceinline__ void rotate32(const ATTN_LDS uint8_t* unit_tile, int lane, const bf16x8 (&h)[2],
+                                         f32x16 (&y)[NA]) {
+    // B operand: lane l holds elements 32a + 16kk + 8(l/32) .. +7 of block l%32
+    const ATTN_LDS uint8_t* p = unit_tile + (lane & 31) * kInRow<NA> + 16 * (lane >> 5);
+    bf16x8 xb[NA][2];
 #pragma unroll
-    for (int h = 1; h < 8; h <<= 1)
+    for (int a = 0; a < NA; ++a)
 #pragma unroll
-        for (int u = 0; u < NU; ++u)
+        for (int kk = 0; kk < 2; ++kk) xb[a][kk] = __builtin_bit_cast(bf16x8, lds_load16(p + 64 * a + 32 * kk));
 #pragma unroll
-            for (int i = 0; i < 8; ++i)
-                if (!(i & h)) {
-                    const float a = x[u][i], b = x[u][i + h];
-                    x[u][i] = a + b;
-                    x[u][i + h] = a - b;
+    for (int a = 0; a < NA; ++a) {
+        y[a] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(h[0], xb[a][0], f32x16{0}, 0, 0, 0);
+        y[a] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(h[1], xb[a][1], y[a], 0, 0, 0);
+    }
+    // y_b = sum_a H_NA[a][b] z_a: butterflies over the chunk index, inside the lane
+#pragma unroll
+    for (int st = 1; st < NA; st <<= 1)
+#pragma unroll
+        for (int a = 0; a < NA; ++a)
+            if (!(a & st)) {
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const float u = y[a][r], v = y[a + st][r];
+                    y[a][r] = u + v;
+                    y[a + st][r] = u - v;
                 }
-    static_assert(LB == 8 || LB == 16, "blocks of 64 or 128 elements");
-    cross_stage<1>(x, t);
-    cross_stage<2>(x, t);
-    cross_stage<4>(x, t);
-    if constexpr (LB == 16) cross_stage<8>(x, t);
+            }
 }
 
-// The 8 bf16 of lane t of block blk as fp32 (zeros past the end; every lane then
-// still takes part in the shuffles).
-__device__ __forceinline__ void load_block(const __bf16* x, int64_t blk, int64_t nblocks, int nb, int t,
-                                           float (&v)[8]) {
-    i32x4 raw = {0, 0, 0, 0};
-    if (blk < nblocks) raw = load16(x + blk * nb + 8 * t);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        v[2 * i] = __int_as_float(raw[i] << 16);
-        v[2 * i + 1] = __int_as_float(raw[i] & (int)0xffff0000);
-    }
+// Orders this wave's LDS writes before its reads of other lanes' data (and the
+// reads before the next writes): LDS operations of one wave complete in order.
+__device__ __forceinline__ void wave_lds_sync() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
 template <int NB>
@@ -111,33 +127,35 @@ constexpr float inv_sqrt_nb() {
 
 __global__ void rq_init(unsigned* cell) { *cell = 0u; }
 
-// Each wave takes U consecutive 1 KiB steps (BPW blocks each, contiguous in
-// memory) and issues all U loads before using any, so every lane keeps U 16-byte
-// loads in flight.
-constexpr int U = 4;
-
 // The max pass runs a fixed grid of grid-stride workgroups: each wave loops over
-// groups of U steps, and each workgroup ends with one reduction and at most one
-// atomic (these are device-scope operations on one address, served beyond the
+// steps of U units of 32 blocks, and each workgroup ends with one reduction and
+// at most one atomic (device-scope operations on one address, served beyond the
 // per-XCD L2s, so their number is kept small).
 constexpr int kAmaxGrid = 2048;
 
 template <int NB>
 __global__ void __launch_bounds__(kThreads) rq_amax(const __bf16* __restrict__ x, int64_t nblocks, unsigned* cell) {
-    constexpr int LB = NB / 8, BPW = 64 / LB;
-    const int lane = threadIdx.x & 63, t = lane % LB;
+    constexpr int NA = NB / 32;
+    __shared__ __attribute__((aligned(16))) uint8_t in_raw[kThreads / 64][U * 32 * kInRow<NA>];
+    const int lane = threadIdx.x & 63;
+    ATTN_LDS uint8_t* tile = (ATTN_LDS uint8_t*)in_raw[threadIdx.x >> 6];
     const int64_t wave = ((int64_t)blockIdx.x * kThreads + threadIdx.x) >> 6;
     const int64_t nwave = ((int64_t)gridDim.x * kThreads) >> 6;
+    const bf16x8 h[2] = {h32_operand(lane, 0), h32_operand(lane, 1)};
     float m = 0.0f;
-    for (int64_t w0 = wave * U; w0 * BPW < nblocks; w0 += nwave * U) {
-        float v[U][8];
+    for (int64_t u0 = wave * U; u0 * 32 < nblocks; u0 += nwave * U) {
+        stage_in<NA>(x, u0, nblocks, lane, tile);
+        wave_lds_sync();
 #pragma unroll
-        for (int u = 0; u < U; ++u) load_block(x, (w0 + u) * BPW + lane / LB, nblocks, NB, t, v[u]);
-        fwht<LB>(v, t);
+        for (int u = 0; u < U; ++u) {
+            f32x16 y[NA];
+            rotate32<NA>(tile + u * 32 * kInRow<NA>, lane, h, y);
 #pragma unroll
-        for (int u = 0; u < U; ++u)
+            for (int a = 0; a < NA; ++a)
 #pragma unroll
-            for (int i = 0; i < 8; ++i) m = fmaxf(m, fabsf(v[u][i]));
+                for (int r = 0; r < 16; ++r) m = fmaxf(m, fabsf(y[a][r]));
+        }
+        wave_lds_sync();
     }
     // max |y| of the normalised rotation: scaling by a positive constant commutes
     // with the maximum, rounding included
@@ -161,27 +179,55 @@ __device__ __forceinline__ float scale_of(float amax) { return amax > 0.0f ? ama
 template <int NB>
 __global__ void __launch_bounds__(kThreads) rq_quant(const __bf16* __restrict__ x, int64_t nblocks,
                                                      const unsigned* cell, uint8_t* __restrict__ out) {
-    constexpr int LB = NB / 8, BPW = 64 / LB;
-    const int lane = threadIdx.x & 63, t = lane % LB;
+    constexpr int NA = NB / 32;
+    // The codes of a unit (32 blocks, contiguous in memory) go through LDS so that the
+    // global stores are whole 16-byte chunks: rows of NB + 16 bytes keep the 16-byte
+    // reads aligned and spread the 4-byte writes over the banks.
+    constexpr int ROW = NB + 16;
+    static_assert(32 * ROW <= U * 32 * kInRow<NA>, "the output staging reuses the input tile");
+    __shared__ __attribute__((aligned(16))) uint8_t in_raw[kThreads / 64][U * 32 * kInRow<NA>];
+    const int lane = threadIdx.x & 63;
+    const int wv = threadIdx.x >> 6;
+    ATTN_LDS uint8_t* tile = (ATTN_LDS uint8_t*)in_raw[wv];
+    ATTN_LDS uint8_t* stage = tile;   // free once every unit's operands are in registers
     const int64_t wave = ((int64_t)blockIdx.x * kThreads + threadIdx.x) >> 6;
-    float v[U][8];
+    const bf16x8 h[2] = {h32_operand(lane, 0), h32_operand(lane, 1)};
+    stage_in<NA>(x, wave * U, nblocks, lane, tile);
+    wave_lds_sync();
+    f32x16 y[U][NA];
 #pragma unroll
-    for (int u = 0; u < U; ++u) load_block(x, (wave * U + u) * BPW + lane / LB, nblocks, NB, t, v[u]);
+    for (int u = 0; u < U; ++u) rotate32<NA>(tile + u * 32 * kInRow<NA>, lane, h, y[u]);
+    wave_lds_sync();
     // one multiply per element by 1/(sqrt(n) scale): within an ulp of dividing the
     // normalised value by the scale, so the rounding to e4m3 can differ only at ties
     const float f = inv_sqrt_nb<NB>() / scale_of(__uint_as_float(*cell));
-    fwht<LB>(v, t);
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-        const int64_t blk = (wave * U + u) * BPW + lane / LB;
-        float q[8];
+        // accumulators 4g..4g+3 of chunk a: columns 32a + 8g + 4(lane/32) + 0..3 of
+        // block lane%32, one 32-bit word of codes
+        ATTN_LDS uint8_t* row = stage + (lane & 31) * ROW + 4 * (lane >> 5);
 #pragma unroll
-        for (int i = 0; i < 8; ++i) q[i] = fminf(fmaxf(v[u][i] * f, -kE4M3Max), kE4M3Max);
-        int w0 = __builtin_amdgcn_cvt_pk_fp8_f32(q[0], q[1], 0, false);
-        w0 = __builtin_amdgcn_cvt_pk_fp8_f32(q[2], q[3], w0, true);
-        int w1 = __builtin_amdgcn_cvt_pk_fp8_f32(q[4], q[5], 0, false);
-        w1 = __builtin_amdgcn_cvt_pk_fp8_f32(q[6], q[7], w1, true);
-        if (blk < nblocks) *reinterpret_cast<int2*>(out + blk * NB + 8 * t) = make_int2(w0, w1);
+        for (int a = 0; a < NA; ++a)
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                float q[4];
+#pragma unroll
+                for (int t = 0; t < 4; ++t) q[t] = fminf(fmaxf(y[u][a][4 * g + t] * f, -kE4M3Max), kE4M3Max);
+                int w = __builtin_amdgcn_cvt_pk_fp8_f32(q[0], q[1], 0, false);
+                w = __builtin_amdgcn_cvt_pk_fp8_f32(q[2], q[3], w, true);
+                *reinterpret_cast<ATTN_LDS int*>(row + 32 * a + 8 * g) = w;
+            }
+        wave_lds_sync();
+        // 16-byte chunk k of the unit's 32 NB contiguous output bytes: block k / (NB/16)
+        const int64_t blk0 = (wave * U + u) * 32;
+#pragma unroll
+        for (int it = 0; it < NB / 32; ++it) {
+            const int k = it * 64 + lane;
+            const int c = k / (NB / 16), col = 16 * (k % (NB / 16));
+            const i32x4 v = lds_load16(stage + c * ROW + col);
+            if (blk0 + c < nblocks) *reinterpret_cast<i32x4*>(out + (blk0 + c) * NB + col) = v;
+        }
+        wave_lds_sync();
     }
 }
 
@@ -192,8 +238,7 @@ __global__ void rq_finish(unsigned* cell) {
 template <int NB>
 hipError_t launch_t(const __bf16* x, uint8_t* x8, unsigned* cell, int64_t n_el, hipStream_t s) {
     const int64_t nblocks = n_el / NB;
-    constexpr int BPW = 64 / (NB / 8);
-    constexpr int64_t per_wg = (int64_t)BPW * U * (kThreads / 64);   // blocks per workgroup
+    constexpr int64_t per_wg = (int64_t)32 * U * (kThreads / 64);   // blocks per workgroup
     hipLaunchKernelGGL(rq_init, dim3(1), dim3(1), 0, s, cell);
     if (nblocks > 0) {
         const int64_t grid = (nblocks + per_wg - 1) / per_wg;
