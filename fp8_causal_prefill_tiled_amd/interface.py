@@ -2,9 +2,10 @@
 
 The pages describe the kernels as a drop-in replacement for ``flash_attn_func``
 ("Zyphra ZYFA: FP8 FlashAttention for AMD MI355X, Up to 1.76x Faster", TL;DR).
-This module gives that calling convention over the C ABI, and registers the two
-attention calls as torch custom operators (``fp8_prefill::attn_fwd_fp8`` and
-``fp8_prefill::attn_fwd_bf16``) with shape-only fake implementations, so that
+This module gives that calling convention (and ``flash_attn_varlen_func``'s)
+over the C ABI, and registers the attention calls as torch custom operators
+(``fp8_prefill::attn_fwd_fp8``, ``fp8_prefill::attn_fwd_bf16`` and their
+``_varlen`` forms) with shape-only fake implementations, so that
 ``torch.compile`` traces them as single opaque nodes instead of breaking the graph.
 
 Every call still runs in the library's HIP kernels through ``binding``; this
@@ -55,6 +56,44 @@ def _attn_fwd_bf16_op(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, softmax
 @_attn_fwd_bf16_op.register_fake
 def _(q, k, v, softmax_scale, causal, with_lse):
     return _fake_outputs(q, v, with_lse)
+
+
+@torch.library.custom_op(f"{_OPS}::attn_fwd_fp8_varlen", mutates_args=(), device_types="cuda")
+def _attn_fwd_fp8_varlen_op(q8: torch.Tensor, k8: torch.Tensor, v8: torch.Tensor, cu_seqlens_q: torch.Tensor,
+                            cu_seqlens_k: torch.Tensor, max_seqlen_q: int, q_scale: float, k_scale: float,
+                            v_scale: float, softmax_scale: float, causal: bool, p_mode: int, with_lse: bool
+                            ) -> tuple[torch.Tensor, torch.Tensor]:
+    res = binding.attn_fwd_fp8_varlen(q8, k8, v8, cu_seqlens_q, max_seqlen_q, q_scale, k_scale, v_scale,
+                                      softmax_scale=softmax_scale if softmax_scale > 0 else None, causal=causal,
+                                      p_mode=p_mode, return_lse=with_lse, cu_seqlens_k=cu_seqlens_k)
+    return res if with_lse else (res, q8.new_empty((0,), dtype=torch.float32))
+
+
+def _fake_varlen_outputs(q, v, with_lse):
+    T, Hq, _ = q.shape
+    return (q.new_empty((T, Hq, v.shape[2]), dtype=torch.bfloat16),
+            q.new_empty((Hq, T) if with_lse else (0,), dtype=torch.float32))
+
+
+@_attn_fwd_fp8_varlen_op.register_fake
+def _(q8, k8, v8, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, q_scale, k_scale, v_scale, softmax_scale, causal,
+      p_mode, with_lse):
+    return _fake_varlen_outputs(q8, v8, with_lse)
+
+
+@torch.library.custom_op(f"{_OPS}::attn_fwd_bf16_varlen", mutates_args=(), device_types="cuda")
+def _attn_fwd_bf16_varlen_op(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, cu_seqlens_q: torch.Tensor,
+                             cu_seqlens_k: torch.Tensor, max_seqlen_q: int, softmax_scale: float, causal: bool,
+                             with_lse: bool) -> tuple[torch.Tensor, torch.Tensor]:
+    res = binding.attn_fwd_bf16_varlen(q, k, v, cu_seqlens_q, max_seqlen_q,
+                                       softmax_scale=softmax_scale if softmax_scale > 0 else None, causal=causal,
+                                       return_lse=with_lse, cu_seqlens_k=cu_seqlens_k)
+    return res if with_lse else (res, q.new_empty((0,), dtype=torch.float32))
+
+
+@_attn_fwd_bf16_varlen_op.register_fake
+def _(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, softmax_scale, causal, with_lse):
+    return _fake_varlen_outputs(q, v, with_lse)
 
 
 def _scale(x, name):
@@ -128,21 +167,22 @@ def flash_attn_varlen_func(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, ma
     """
     if dropout_p != 0.0 or tuple(window_size) != (-1, -1) or softcap != 0.0 or alibi_slopes is not None:
         raise NotImplementedError("dropout, sliding windows, softcapping and ALiBi are not supported")
+    sm = 0.0 if softmax_scale is None else float(softmax_scale)
     if q.dtype in _FP8_DTYPES:
         if k.dtype not in _FP8_DTYPES or v.dtype not in _FP8_DTYPES:
             raise TypeError("q, k and v must all be FP8 e4m3 (or all bfloat16)")
         q8, k8, v8 = (t.view(torch.uint8) if t.dtype != torch.uint8 else t for t in (q, k, v))
-        res = binding.attn_fwd_fp8_varlen(q8, k8, v8, cu_seqlens_q, max_seqlen_q, _scale(q_descale, "q_descale"),
-                                          _scale(k_descale, "k_descale"), _scale(v_descale, "v_descale"),
-                                          softmax_scale=softmax_scale, causal=causal, p_mode=p_mode,
-                                          return_lse=return_attn_probs, cu_seqlens_k=cu_seqlens_k)
+        out, lse = _attn_fwd_fp8_varlen_op(q8, k8, v8, cu_seqlens_q, cu_seqlens_k, int(max_seqlen_q),
+                                           _scale(q_descale, "q_descale"), _scale(k_descale, "k_descale"),
+                                           _scale(v_descale, "v_descale"), sm, bool(causal),
+                                           int(binding._P_MODES[p_mode]), bool(return_attn_probs))
     elif q.dtype == torch.bfloat16:
         if k.dtype != torch.bfloat16 or v.dtype != torch.bfloat16:
             raise TypeError("q, k and v must all be bfloat16 (or all FP8 e4m3)")
-        res = binding.attn_fwd_bf16_varlen(q, k, v, cu_seqlens_q, max_seqlen_q, softmax_scale=softmax_scale,
-                                           causal=causal, return_lse=return_attn_probs, cu_seqlens_k=cu_seqlens_k)
+        out, lse = _attn_fwd_bf16_varlen_op(q, k, v, cu_seqlens_q, cu_seqlens_k, int(max_seqlen_q), sm, bool(causal),
+                                            bool(return_attn_probs))
     else:
         raise TypeError(f"unsupported input dtype {q.dtype}: bfloat16 or float8_e4m3fn")
     if return_attn_probs:
-        return res[0], res[1], None
-    return res
+        return out, lse, None
+    return out

@@ -94,3 +94,26 @@ def test_varlen_wrapper_matches_binding():
     torch.cuda.synchronize()
     assert torch.equal(out.view(torch.int16), ref.view(torch.int16)) and torch.equal(lse, ref_lse)
     assert torch.equal(out8.view(torch.int16), ref8.view(torch.int16))
+
+
+def test_varlen_opcheck_and_compile():
+    from fp8_causal_prefill_tiled_amd.interface import (flash_attn_varlen_func, _attn_fwd_bf16_varlen_op,
+                                                         _attn_fwd_fp8_varlen_op)
+    g = torch.Generator().manual_seed(6)
+    q = torch.randn((96, 4, 128), generator=g).to(torch.bfloat16).to(DEV)
+    k = torch.randn((160, 2, 128), generator=g).to(torch.bfloat16).to(DEV)
+    cq = torch.tensor([0, 40, 96], dtype=torch.int32, device=DEV)
+    ck = torch.tensor([0, 100, 160], dtype=torch.int32, device=DEV)
+    torch.library.opcheck(_attn_fwd_bf16_varlen_op, (q, k, k, cq, ck, 56, 0.0, True, True))
+    q8, qs = W.quantize_e4m3(q.float().cpu())
+    k8, ks = W.quantize_e4m3(k.float().cpu())
+    q8, k8 = q8.to(DEV), k8.to(DEV)
+    torch.library.opcheck(_attn_fwd_fp8_varlen_op, (q8, k8, k8, cq, ck, 56, qs, ks, ks, 0.0, False, 1, True))
+
+    def f(q, k, cq, ck):
+        return flash_attn_varlen_func(q, k, k, cq, ck, 56, 100, causal=True).float() * 2
+
+    eager = f(q, k, cq, ck)
+    compiled = torch.compile(f, backend="aot_eager", fullgraph=True)(q, k, cq, ck)
+    torch.cuda.synchronize()
+    assert torch.equal(eager, compiled)

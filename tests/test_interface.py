@@ -65,3 +65,24 @@ def test_dtype_and_scale_errors():
             flash_attn_func(q, kb, vb)
         with pytest.raises(TypeError):
             flash_attn_func(qb.half(), kb.half(), vb.half())
+
+
+@pytest.mark.parametrize("dtype,op", [(torch.bfloat16, "fp8_prefill.attn_fwd_bf16_varlen"),
+                                      (torch.float8_e4m3fn, "fp8_prefill.attn_fwd_fp8_varlen")])
+def test_varlen_traces_as_one_custom_op_node(dtype, op):
+    from fp8_causal_prefill_tiled_amd.interface import flash_attn_varlen_func
+    kw = dict(q_descale=0.5, k_descale=0.25, v_descale=1.0) if dtype != torch.bfloat16 else {}
+
+    def f(q, k, v, cq, ck):
+        out, lse, _ = flash_attn_varlen_func(q, k, v, cq, ck, 64, 96, causal=True, return_attn_probs=True, **kw)
+        return out, lse
+
+    with FakeTensorMode():
+        q = torch.empty(100, 4, 128, dtype=dtype, device="cuda")
+        k = torch.empty(150, 2, 128, dtype=dtype, device="cuda")
+        cq = torch.empty(3, dtype=torch.int32, device="cuda")
+        g = make_fx(f, tracing_mode="fake")(q, k, k, cq, cq)
+        out, lse = f(q, k, k, cq, cq)
+    assert out.shape == (100, 4, 128) and out.dtype == torch.bfloat16 and lse.shape == (4, 100)
+    targets = [str(n.target) for n in g.graph.nodes if n.op == "call_function"]
+    assert sum(t.startswith(op) for t in targets) == 1, targets
