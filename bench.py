@@ -266,13 +266,16 @@ def input_study(w, d, q, k, v, out, stream, flops, steps, warmup, modes, paths):
     return res
 
 
-def cpu_baseline(w, d, out_gpu, seconds, dtype):
+def cpu_baseline(w, d, outs, seconds, dtype):
     """Time the CPU oracle (fp64 attention) on a bounded sample of the same workload and
-    compare the GPU output on those rows.  Returns the cpu_baseline object.
+    compare the GPU outputs on those rows.  Returns the cpu_baseline object.
 
+    outs: {path: GPU output as a float array}, the headline path first.
     Sample: query rows spread over 0..S-1 (every 64th row, longest causal prefixes first, then
     the next residue), in chunks of 64, for three heads, until about `seconds` of oracle time
-    has been spent."""
+    has been spent.  The GPU error is measured against fp64 attention on the dequantised inputs
+    (the method's own error) and, for FP8, also on the unquantised fp32 draws (input quantisation
+    included); only the first is timed."""
     import numpy as np
     from threadpoolctl import threadpool_info
     from oracle.attention64 import attention_fp64, dequantize
@@ -291,8 +294,15 @@ def cpu_baseline(w, d, out_gpu, seconds, dtype):
         else:
             per_head.append((h, d["q"][:, :, h:h + 1].float().numpy(), d["k"][:, :, g:g + 1].float().numpy(),
                              d["v"][:, :, g:g + 1].float().numpy()))
+    raw = None
+    if dtype == "fp8":
+        from fp8_causal_prefill_tiled_amd import workloads as W
+        q32, k32, v32 = W.draw_fp32(w)          # the same seeded draws the codes were quantised from
+        raw = {h: (q32[:, :, h:h + 1].numpy(), k32[:, :, h // (w.Hq // w.Hkv):h // (w.Hq // w.Hkv) + 1].numpy(),
+                   v32[:, :, h // (w.Hq // w.Hkv):h // (w.Hq // w.Hkv) + 1].numpy()) for h in heads}
+        del q32, k32, v32
     flops, el, nrows = 0.0, 0.0, 0
-    errs_num, errs_den = 0.0, 0.0
+    err = {m: {"deq": [0.0, 0.0], "raw": [0.0, 0.0], "head": {h: [0.0, 0.0] for h in heads}} for m in outs}
     i = 0
     while el < seconds and i < len(order):
         rows = np.sort(order[i:i + 64])
@@ -303,9 +313,23 @@ def cpu_baseline(w, d, out_gpu, seconds, dtype):
             ref = attention_fp64(q, k, v, rows=rows)
             el += time.perf_counter() - t0
             flops += float(np.sum(2.0 * (rows + 1) * (w.d_qk + w.d_v)))
-            got = out_gpu[:, rows, h:h + 1].astype(np.float64)
-            errs_num += float(np.sum((got - ref) ** 2))
-            errs_den += float(np.sum(ref ** 2))
+            ref_raw = attention_fp64(*raw[h], rows=rows) if raw is not None else None
+            for m, out_gpu in outs.items():
+                got = out_gpu[:, rows, h:h + 1].astype(np.float64)
+                e2, r2 = float(np.sum((got - ref) ** 2)), float(np.sum(ref ** 2))
+                for acc in (err[m]["deq"], err[m]["head"][h]):
+                    acc[0] += e2
+                    acc[1] += r2
+                if ref_raw is not None:
+                    err[m]["raw"][0] += float(np.sum((got - ref_raw) ** 2))
+                    err[m]["raw"][1] += float(np.sum(ref_raw ** 2))
+
+    def rel(a):
+        return float(np.sqrt(a[0] / a[1])) if a[1] > 0 else None
+    errors = {m: {"rel_rms_vs_fp64_dequantised_inputs": rel(e["deq"]),
+                  "rel_rms_vs_fp64_unquantised_inputs": rel(e["raw"]) if raw is not None else None,
+                  "per_head_max_rel_rms_dequantised": max(rel(v) for v in e["head"].values())}
+              for m, e in err.items()}
     tiny = _cpu_tiny_full()
     return {
         "value": flops / el / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
@@ -313,7 +337,8 @@ def cpu_baseline(w, d, out_gpu, seconds, dtype):
         "sample": f"fp64 attention (oracle/attention64.py, numpy+BLAS) on {nrows} query rows "
                   f"(spread over 0..S-1, longest prefixes first) x heads {heads} of the {w.name} workload, "
                   f"{el:.1f} s of oracle time; FLOPs counted 2*(i+1)*(d_qk+d_v) per row i",
-        "gpu_rel_rms_vs_oracle_on_sample": float(np.sqrt(errs_num / errs_den)),
+        "gpu_rel_rms_vs_oracle_on_sample": errors[next(iter(outs))]["rel_rms_vs_fp64_dequantised_inputs"],
+        "gpu_error_on_sample": errors,
         "cpu_model": _cpu_model(),
         "os_cpu_count": os.cpu_count(),
     }
@@ -423,8 +448,14 @@ def main():
 
     cpu = None
     if not args.no_cpu_baseline:
-        out_np = out.float().cpu().numpy()
-        cpu = cpu_baseline(w, d, out_np, args.cpu_seconds, args.dtype)
+        outs = {modes[0]: out.float().cpu().numpy()}
+        for m in modes[1:]:                       # the other probability path, one more launch
+            o2 = torch.empty_like(out)
+            binding.attn_fwd_fp8(q, k, v, d["q_scale"], d["k_scale"], d["v_scale"], p_mode=m, out=o2, stream=stream)
+            torch.cuda.synchronize()
+            outs[m] = o2.float().cpu().numpy()
+            del o2
+        cpu = cpu_baseline(w, d, outs, args.cpu_seconds, args.dtype)
 
     rot = None
     if args.dtype == "fp8" and not args.no_rotate:

@@ -26,3 +26,22 @@ def test_sampler_without_sysfs_reports_none():
     s.power, s.clock, s.power_file, s.clock_file, s.dpm_file, s.power_cap_w = [], [], None, None, None, None
     r = s.summary(1e12, 1.0)
     assert r["power_w_avg"] is None and r["tflop_per_joule"] is None
+
+
+def test_cpu_baseline_reports_both_paths_errors_on_a_small_workload():
+    import numpy as np
+    from fp8_causal_prefill_tiled_amd import workloads as W
+    from oracle.attention64 import attention_fp64, dequantize
+    w = W.WORKLOADS["tiny"]
+    d = W.make_fp8(w)
+    ref = attention_fp64(*(dequantize(d[n + "8"].numpy(), d[n + "_scale"]) for n in ("q", "k", "v")))
+    rng = np.random.default_rng(0)
+    outs = {"lean": ref * (1 + 0.01 * rng.standard_normal(ref.shape)), "exact": ref.copy()}
+    r = bench.cpu_baseline(w, d, outs, 0.05, "fp8")
+    e = r["gpu_error_on_sample"]
+    assert r["kind"] == "oracle" and r["value"] > 0 and r["cores"] >= 1
+    assert 0.005 < e["lean"]["rel_rms_vs_fp64_dequantised_inputs"] < 0.02
+    assert e["exact"]["rel_rms_vs_fp64_dequantised_inputs"] < 1e-12   # same rows, chunked differently
+    # against the unquantised draws the error includes the e4m3 input rounding
+    assert e["exact"]["rel_rms_vs_fp64_unquantised_inputs"] > 0.005
+    assert r["gpu_rel_rms_vs_oracle_on_sample"] == e["lean"]["rel_rms_vs_fp64_dequantised_inputs"]
