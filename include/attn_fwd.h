@@ -1,6 +1,7 @@
 /*
- * attn_fwd.h - C ABI of libattnfwd.so: causal forward prefill attention on
- * AMD Instinct MI355X (CDNA4, gfx950).
+ * attn_fwd.h - C ABI of libattnfwd.so: forward prefill attention (causal or
+ * not, equal-length or variable-length batches) on AMD Instinct MI355X (CDNA4,
+ * gfx950), and the Hadamard rotation + FP8 quantisation of its Q and K.
  *
  * Operation (every attention entry point): for every batch b, query head h and
  * query position i < S,
