@@ -40,7 +40,7 @@ def test_tiny_full_tensor(mode):
 @pytest.mark.parametrize("shape", [
     (1, 2, 2, 1, 128), (1, 2, 1, 2, 128), (1, 2, 2, 63, 128), (1, 2, 2, 64, 128), (1, 2, 2, 65, 128),
     (2, 4, 2, 129, 128), (1, 4, 1, 200, 192), (1, 2, 2, 333, 128), (2, 4, 4, 515, 192),
-    (1, 8, 2, 1000, 128),
+    (1, 8, 2, 1000, 128), (1, 64, 2, 300, 128), (3, 16, 16, 70, 192), (1, 32, 1, 257, 192),
 ])
 def test_ragged_and_gqa_full_tensor(shape, mode):
     B, Hq, Hkv, S, dqk = shape
