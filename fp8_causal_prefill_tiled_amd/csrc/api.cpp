@@ -48,8 +48,11 @@ int check_common(const void* q, const void* k, const void* v, void* o, const flo
     if (d_v != 128) return fail(ATTN_E_UNSUPPORTED, "%s: d_v=%d unsupported (128)", who, d_v);
     // Every element offset is formed in 64-bit arithmetic by the kernels; the row
     // index and the head count must fit comfortably in 32-bit integers.
-    const int64_t most = std::max<int64_t>(std::max<int64_t>(rows, rows_k), (int64_t)B * S);
+    const int64_t most = std::max<int64_t>(rows, rows_k);
     if (most > (int64_t)1 << 30) return fail(ATTN_E_UNSUPPORTED, "%s: %lld rows too many", who, (long long)most);
+    // one workgroup per (256-query tile, sequence, head)
+    const int64_t grid = ((int64_t)S + 255) / 256 * B * Hq;
+    if (grid > 0x7fffffffLL) return fail(ATTN_E_UNSUPPORTED, "%s: %lld workgroups too many", who, (long long)grid);
     if (B == 0 || S == 0 || rows == 0) return -1;
     if (!q || !k || !v || !o) return fail(ATTN_E_INVALID_ARG, "%s: null tensor pointer", who);
     if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o))

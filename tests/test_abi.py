@@ -139,6 +139,7 @@ OK_IF_NULL_K = "ok-if-null-k"
     (dict(total_q=-1), INVALID), (dict(total_k=-1), INVALID), (dict(max_seqlen_q=-1), INVALID),
     (dict(n_seqs=-1), INVALID),
     (dict(total_q=(1 << 30) + 1), UNSUPPORTED), (dict(total_k=(1 << 30) + 1), UNSUPPORTED),
+    (dict(n_seqs=1 << 22, max_seqlen_q=1 << 12, Hq=64, Hkv=2), UNSUPPORTED),   # grid beyond 2^31 workgroups
     (dict(cu_seqlens_k=0, total_k=-5), OK_IF_NULL_K),       # null key offsets: total_k ignored
     (dict(k=O + 4096), INVALID),                            # K starting inside O
     (dict(d_qk=64), UNSUPPORTED), (dict(Hq=3), INVALID), (dict(causal=2), INVALID),
