@@ -19,7 +19,7 @@ ATTN_OK, ATTN_E_INVALID_ARG, ATTN_E_UNSUPPORTED, ATTN_E_HIP = 0, 1, 2, 3
 P_EXACT, P_LEAN = 0, 1
 _P_MODES = {"exact": P_EXACT, "lean": P_LEAN, P_EXACT: P_EXACT, P_LEAN: P_LEAN}
 
-_EXPORTS = ("attn_fwd_fp8", "attn_fwd_fp8_lse", "attn_fwd_fp8_varlen", "attn_fwd_bf16", "attn_fwd_bf16_lse",
+_EXPORTS = ("attn_fwd_fp8", "attn_fwd_fp8_lse", "attn_fwd_fp8_varlen", "attn_fwd_fp8_dscale", "attn_fwd_bf16", "attn_fwd_bf16_lse",
             "attn_fwd_bf16_varlen", "attn_rotate_quant_bf16", "attn_last_error", "attn_abi_version")
 
 
@@ -49,6 +49,8 @@ def load_library():
     lib.attn_fwd_fp8.restype = i
     lib.attn_fwd_fp8_lse.argtypes = [vp, vp, vp, vp, vp, f, f, f, f, i, i, i, i, i, i, i, i, vp]
     lib.attn_fwd_fp8_lse.restype = i
+    lib.attn_fwd_fp8_dscale.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, f, i, i, i, i, i, i, i, i, vp]
+    lib.attn_fwd_fp8_dscale.restype = i
     lib.attn_fwd_bf16.argtypes = [vp, vp, vp, vp, f, i, i, i, i, i, i, i, vp]
     lib.attn_fwd_bf16.restype = i
     lib.attn_fwd_bf16_lse.argtypes = [vp, vp, vp, vp, vp, f, i, i, i, i, i, i, i, vp]
@@ -111,6 +113,13 @@ def attn_fwd_fp8_lse_raw(q, k, v, o, lse, q_scale, k_scale, v_scale, softmax_sca
                                            B, Hq, Hkv, S, d_qk, d_v, causal, p_mode, stream)
 
 
+def attn_fwd_fp8_dscale_raw(q, k, v, o, lse, q_scale, k_scale, v_scale, softmax_scale, B, Hq, Hkv, S, d_qk, d_v,
+                            causal, p_mode, stream=0):
+    """Direct C call with the three scales as device pointers."""
+    return load_library().attn_fwd_fp8_dscale(q, k, v, o, lse, q_scale, k_scale, v_scale, softmax_scale,
+                                              B, Hq, Hkv, S, d_qk, d_v, causal, p_mode, stream)
+
+
 def attn_fwd_bf16_raw(q, k, v, o, softmax_scale, B, Hq, Hkv, S, d_qk, d_v, causal, stream=0):
     return load_library().attn_fwd_bf16(q, k, v, o, softmax_scale, B, Hq, Hkv, S, d_qk, d_v, causal, stream)
 
@@ -167,6 +176,9 @@ def attn_fwd_fp8(q8, k8, v8, q_scale, k_scale, v_scale, softmax_scale=None, caus
     Returns the bf16 output (B, S, Hq, d_v), enqueued on ``stream`` (default:
     torch's current stream of the inputs' device); with ``return_lse`` returns
     (out, lse), lse the fp32 (B, Hq, S) natural-log normaliser of every row.
+    The scales are floats, or one-element float32 GPU tensors (all three), which
+    the kernel reads when it runs - e.g. the scales rotate_quant_bf16 wrote on the
+    same stream, with no host synchronisation.
     """
     for t, n in ((q8, "q8"), (k8, "k8"), (v8, "v8")):
         if t.dtype not in (torch.uint8, torch.float8_e4m3fn):
@@ -182,6 +194,19 @@ def attn_fwd_fp8(q8, k8, v8, q_scale, k_scale, v_scale, softmax_scale=None, caus
         raise ValueError("out must be a contiguous bf16 tensor of shape (B, S, Hq, d_v)")
     sm = 0.0 if softmax_scale is None else float(softmax_scale)
     lse = _lse_out(return_lse, B, Hq, S, q8.device)
+    dev_scales = [isinstance(x, torch.Tensor) for x in (q_scale, k_scale, v_scale)]
+    if any(dev_scales):
+        if not all(dev_scales):
+            raise TypeError("q_scale, k_scale and v_scale must be all floats or all device tensors")
+        for x in (q_scale, k_scale, v_scale):
+            if not x.is_cuda or x.dtype != torch.float32 or x.numel() != 1 or not x.is_contiguous():
+                raise ValueError("device scales must be one-element contiguous float32 GPU tensors")
+        st = attn_fwd_fp8_dscale_raw(q8.data_ptr(), k8.data_ptr(), v8.data_ptr(), out.data_ptr(),
+                                     0 if lse is None else lse.data_ptr(), q_scale.data_ptr(), k_scale.data_ptr(),
+                                     v_scale.data_ptr(), sm, B, Hq, Hkv, S, dqk, dv, int(bool(causal)),
+                                     _P_MODES[p_mode], _stream_ptr(stream, q8.device))
+        _check(st)
+        return (out, lse) if return_lse else out
     st = attn_fwd_fp8_lse_raw(q8.data_ptr(), k8.data_ptr(), v8.data_ptr(), out.data_ptr(),
                               0 if lse is None else lse.data_ptr(),
                               float(q_scale), float(k_scale), float(v_scale), sm,

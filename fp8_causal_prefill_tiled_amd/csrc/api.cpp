@@ -83,7 +83,7 @@ int check_cu(const int* cu, int n_seqs, const char* who) {
 }
 
 int run_fp8(const void* q, const void* k, const void* v, void* o, float* lse, bool varlen, const int* cu, int total,
-            const int* cu_k, int total_k,
+            const int* cu_k, int total_k, const float* dq, const float* dk, const float* dv,
             float q_scale, float k_scale, float v_scale, float softmax_scale, int B, int Hq, int Hkv, int S,
             int d_qk, int d_v, int causal, int p_mode, hipStream_t stream, const char* who) {
     const int64_t rows = varlen ? (int64_t)total : (int64_t)B * S;
@@ -91,16 +91,26 @@ int run_fp8(const void* q, const void* k, const void* v, void* o, float* lse, bo
     int st = check_common(q, k, v, o, lse, softmax_scale, B, Hq, Hkv, S, rows, rows_k, d_qk, d_v, causal, 1, who);
     if (st == -1) { g_err[0] = 0; return ATTN_OK; }
     if (st != ATTN_OK) return st;
-    if (!(std::isfinite(q_scale) && q_scale > 0.f) || !(std::isfinite(k_scale) && k_scale > 0.f) ||
-        !(std::isfinite(v_scale) && v_scale > 0.f))
+    const bool dscale = dq != nullptr;
+    if (dscale) {
+        if (!dk || !dv) return fail(ATTN_E_INVALID_ARG, "%s: null scale pointer", who);
+        const float* sp[3] = {dq, dk, dv};
+        for (const float* x : sp)
+            if ((reinterpret_cast<uintptr_t>(x) & 3u) != 0)
+                return fail(ATTN_E_INVALID_ARG, "%s: scale pointers must be 4-byte aligned", who);
+    } else if (!(std::isfinite(q_scale) && q_scale > 0.f) || !(std::isfinite(k_scale) && k_scale > 0.f) ||
+               !(std::isfinite(v_scale) && v_scale > 0.f)) {
         return fail(ATTN_E_INVALID_ARG, "%s: q/k/v scales must be finite and > 0", who);
+    }
     if (p_mode != ATTN_P_EXACT && p_mode != ATTN_P_LEAN)
         return fail(ATTN_E_INVALID_ARG, "%s: p_mode=%d must be 0 (exact) or 1 (lean)", who, p_mode);
     attnfwd::Problem p{q, k, v, o, q_scale, k_scale, v_scale,
                        softmax_scale > 0.f ? softmax_scale : 1.0f / std::sqrt((float)d_qk),
-                       B, Hq, Hkv, S, d_qk, d_v, p_mode, stream, lse, causal, cu, (int)rows, cu_k, (int)rows_k};
+                       B, Hq, Hkv, S, d_qk, d_v, p_mode, stream, lse, causal, cu, (int)rows, cu_k, (int)rows_k,
+                       dq, dk, dv};
     const double c = (double)q_scale * k_scale * p.sm * 1.4426950408889634;
-    if (!(c < 1e30 && c > 1e-30)) return fail(ATTN_E_INVALID_ARG, "%s: q_scale*k_scale*softmax_scale out of range", who);
+    if (!dscale && !(c < 1e30 && c > 1e-30))
+        return fail(ATTN_E_INVALID_ARG, "%s: q_scale*k_scale*softmax_scale out of range", who);
     return finish(attnfwd::launch_fp8(p), who);
 }
 
@@ -133,7 +143,7 @@ int attn_fwd_fp8_lse(const void* q, const void* k, const void* v, void* o, float
                      float q_scale, float k_scale, float v_scale, float softmax_scale,
                      int B, int Hq, int Hkv, int S, int d_qk, int d_v,
                      int causal, int p_mode, hipStream_t stream) {
-    return run_fp8(q, k, v, o, lse, false, nullptr, 0, nullptr, 0, q_scale, k_scale, v_scale, softmax_scale, B, Hq, Hkv, S, d_qk, d_v,
+    return run_fp8(q, k, v, o, lse, false, nullptr, 0, nullptr, 0, nullptr, nullptr, nullptr, q_scale, k_scale, v_scale, softmax_scale, B, Hq, Hkv, S, d_qk, d_v,
                    causal, p_mode, stream, lse ? "attn_fwd_fp8_lse" : "attn_fwd_fp8");
 }
 
@@ -154,8 +164,19 @@ int attn_fwd_fp8_varlen(const void* q, const void* k, const void* v, void* o, fl
     if (int st = check_cu(cu_seqlens_q, n_seqs, who)) return st;
     if (int st = check_cu(cu_seqlens_k, 0, who)) return st;
     const int* cu_k = cu_seqlens_k ? cu_seqlens_k : cu_seqlens_q;
-    return run_fp8(q, k, v, o, lse, true, cu_seqlens_q, total_q, cu_k, cu_seqlens_k ? total_k : total_q, q_scale, k_scale,
+    return run_fp8(q, k, v, o, lse, true, cu_seqlens_q, total_q, cu_k, cu_seqlens_k ? total_k : total_q,
+                   nullptr, nullptr, nullptr, q_scale, k_scale,
                    v_scale, softmax_scale, n_seqs, Hq, Hkv, max_seqlen_q, d_qk, d_v, causal, p_mode, stream, who);
+}
+
+int attn_fwd_fp8_dscale(const void* q, const void* k, const void* v, void* o, float* lse,
+                        const float* q_scale, const float* k_scale, const float* v_scale, float softmax_scale,
+                        int B, int Hq, int Hkv, int S, int d_qk, int d_v, int causal, int p_mode,
+                        hipStream_t stream) {
+    const char* who = "attn_fwd_fp8_dscale";
+    if (!q_scale || !k_scale || !v_scale) return fail(ATTN_E_INVALID_ARG, "%s: null scale pointer", who);
+    return run_fp8(q, k, v, o, lse, false, nullptr, 0, nullptr, 0, q_scale, k_scale, v_scale, 1.f, 1.f, 1.f,
+                   softmax_scale, B, Hq, Hkv, S, d_qk, d_v, causal, p_mode, stream, who);
 }
 
 int attn_fwd_bf16_lse(const void* q, const void* k, const void* v, void* o, float* lse, float softmax_scale,
@@ -201,6 +222,6 @@ int attn_rotate_quant_bf16(const void* x, void* x8, float* scale, int B, int S, 
 
 const char* attn_last_error(void) { return g_err; }
 
-int attn_abi_version(void) { return 103; }
+int attn_abi_version(void) { return 104; }
 
 }  // extern "C"

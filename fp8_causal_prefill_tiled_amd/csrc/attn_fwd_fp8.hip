@@ -64,6 +64,10 @@ struct Fp8Params {
     int total;        // variable-length batches: rows of the packed Q and O
     const int* cu_k;  // variable-length batches: B + 1 key row offsets (device)
     int total_k;      // variable-length batches: rows of the packed K and V
+    const float* dq;  // per-tensor scales in device memory (one float each), or null:
+    const float* dk;  //   then c, a8 and v_scale above are used as given
+    const float* dv;
+    float sm;         // softmax scale (for scales read from device memory)
 };
 
 // 16-byte chunk swizzle of a V row in LDS.  The transposing read of one 16-lane
@@ -100,7 +104,7 @@ __device__ __forceinline__ int v_swz(int row) { return (row & 3) | (((row >> 3) 
 // workgroup with the transposing ds_read_b64_tr_b8, far slower per byte than
 // ds_read_b128 on gfx950.  Buffer loads use a range ending at row S, so rows
 // past S read as zeros.
-template <int DQK, int PMODE, bool CAUSAL, bool LSE, bool VARLEN>
+template <int DQK, int PMODE, bool CAUSAL, bool LSE, bool VARLEN, bool DSCALE>
 __global__ void __launch_bounds__(512) fp8_causal_fwd(Fp8Params a) {
     using T = Fp8Tile<DQK>;
     constexpr int NT = 256;                       // threads per group
@@ -159,6 +163,17 @@ __global__ void __launch_bounds__(512) fp8_causal_fwd(Fp8Params a) {
     const int c = lane & 31;
     const int hh = lane >> 5;
     const int qabs = q0 + 32 * w + c;             // query of this lane
+
+    // The scales: by value, or read from device memory where an earlier kernel on the
+    // stream (the rotation's quantisation) wrote them; the same double-precision
+    // formula as the host's, so both give the same bits.
+    float sc_c = a.c, sc_a8 = a.a8, sc_v = a.v_scale;
+    if constexpr (DSCALE) {
+        const double cd = (double)*a.dq * (double)*a.dk * (double)a.sm * 1.4426950408889634;
+        sc_c = (float)cd;
+        sc_a8 = (float)(8.0 * cd);
+        sc_v = *a.dv;
+    }
 
     const int64_t q_row = (int64_t)a.Hq * DQK;
     const int k_row = a.Hkv * DQK;                // bytes between consecutive keys
@@ -329,7 +344,7 @@ __global__ void __launch_bounds__(512) fp8_causal_fwd(Fp8Params a) {
     };
     auto prep_exponent = [&]() {
         const float mx = pair_max(mx_n);
-        const float M = fmaxf(ceilf(mx * a.c), -1.0e30f);  // floor: rows with no visible key here
+        const float M = fmaxf(ceilf(mx * sc_c), -1.0e30f);  // floor: rows with no visible key here
         bias_n = PMODE == 0 ? 8.0f - M : 120.0f - 8.0f * M;
         need_n = M > ref + kRefSlack;
         nref_n = need_n ? M : ref;
@@ -349,10 +364,10 @@ __global__ void __launch_bounds__(512) fp8_causal_fwd(Fp8Params a) {
             for (int q4 = 0; q4 < 8; ++q4) {
                 const f32x16& x = q4 < 4 ? s0 : s1;
                 const int e = 4 * (q4 & 3);
-                const float p0 = __builtin_amdgcn_exp2f(fmaf(x[e + 0], a.c, bias_n));
-                const float p1 = __builtin_amdgcn_exp2f(fmaf(x[e + 1], a.c, bias_n));
-                const float p2 = __builtin_amdgcn_exp2f(fmaf(x[e + 2], a.c, bias_n));
-                const float p3 = __builtin_amdgcn_exp2f(fmaf(x[e + 3], a.c, bias_n));
+                const float p0 = __builtin_amdgcn_exp2f(fmaf(x[e + 0], sc_c, bias_n));
+                const float p1 = __builtin_amdgcn_exp2f(fmaf(x[e + 1], sc_c, bias_n));
+                const float p2 = __builtin_amdgcn_exp2f(fmaf(x[e + 2], sc_c, bias_n));
+                const float p3 = __builtin_amdgcn_exp2f(fmaf(x[e + 3], sc_c, bias_n));
                 const int wd = __builtin_amdgcn_cvt_pk_fp8_f32(p0, p1, 0, false);
                 pw[q4] = __builtin_amdgcn_cvt_pk_fp8_f32(p2, p3, wd, true);
             }
@@ -362,10 +377,10 @@ __global__ void __launch_bounds__(512) fp8_causal_fwd(Fp8Params a) {
                 const f32x16& x = q4 < 4 ? s0 : s1;
                 const int e = 4 * (q4 & 3);
                 unsigned wd = 0;
-                wd = __builtin_amdgcn_cvt_pk_u8_f32(fmaf(x[e + 0], a.a8, bias_n), 0, wd);
-                wd = __builtin_amdgcn_cvt_pk_u8_f32(fmaf(x[e + 1], a.a8, bias_n), 1, wd);
-                wd = __builtin_amdgcn_cvt_pk_u8_f32(fmaf(x[e + 2], a.a8, bias_n), 2, wd);
-                wd = __builtin_amdgcn_cvt_pk_u8_f32(fmaf(x[e + 3], a.a8, bias_n), 3, wd);
+                wd = __builtin_amdgcn_cvt_pk_u8_f32(fmaf(x[e + 0], sc_a8, bias_n), 0, wd);
+                wd = __builtin_amdgcn_cvt_pk_u8_f32(fmaf(x[e + 1], sc_a8, bias_n), 1, wd);
+                wd = __builtin_amdgcn_cvt_pk_u8_f32(fmaf(x[e + 2], sc_a8, bias_n), 2, wd);
+                wd = __builtin_amdgcn_cvt_pk_u8_f32(fmaf(x[e + 3], sc_a8, bias_n), 3, wd);
                 pw[q4] = (int)wd;
             }
         }
@@ -503,10 +518,10 @@ __global__ void __launch_bounds__(512) fp8_causal_fwd(Fp8Params a) {
         for (int dt = 0; dt < 4; ++dt) {
 #pragma unroll
             for (int r4 = 0; r4 < 4; ++r4) {
-                float x0 = (o[dt][4 * r4 + 0] / l0d) * a.v_scale;
-                float x1 = (o[dt][4 * r4 + 1] / l0d) * a.v_scale;
-                float x2 = (o[dt][4 * r4 + 2] / l0d) * a.v_scale;
-                float x3 = (o[dt][4 * r4 + 3] / l0d) * a.v_scale;
+                float x0 = (o[dt][4 * r4 + 0] / l0d) * sc_v;
+                float x1 = (o[dt][4 * r4 + 1] / l0d) * sc_v;
+                float x2 = (o[dt][4 * r4 + 2] / l0d) * sc_v;
+                float x3 = (o[dt][4 * r4 + 3] / l0d) * sc_v;
                 uint2 pk = make_uint2(pack_bf16x2(x0, x1), pack_bf16x2(x2, x3));
                 *reinterpret_cast<uint2*>(op + 32 * dt + 8 * r4 + 4 * hh) = pk;
             }
@@ -514,7 +529,7 @@ __global__ void __launch_bounds__(512) fp8_causal_fwd(Fp8Params a) {
     }
 }
 
-template <int DQK, int PMODE, bool CAUSAL, bool LSE, bool VARLEN>
+template <int DQK, int PMODE, bool CAUSAL, bool LSE, bool VARLEN, bool DSCALE>
 hipError_t launch_t(const Problem& p) {
     constexpr int NW = 8;
     constexpr int BM = 256;
@@ -536,32 +551,43 @@ hipError_t launch_t(const Problem& p) {
     a.total = p.total;
     a.cu_k = p.cu_k;
     a.total_k = p.total_k;
+    a.dq = p.dq;
+    a.dk = p.dk;
+    a.dv = p.dv;
+    a.sm = p.sm;
     a.n_tiles = (p.S + BM - 1) / BM;
     const long long nblocks = (long long)a.n_tiles * p.B * p.Hq;
     if (nblocks <= 0 || nblocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-    hipLaunchKernelGGL((fp8_causal_fwd<DQK, PMODE, CAUSAL, LSE, VARLEN>), dim3((unsigned)nblocks), dim3(NW * 64), 0, p.stream, a);
+    hipLaunchKernelGGL((fp8_causal_fwd<DQK, PMODE, CAUSAL, LSE, VARLEN, DSCALE>), dim3((unsigned)nblocks), dim3(NW * 64), 0, p.stream, a);
     return hipGetLastError();
 }
 
 // The log-sum-exp store is a template switch: the kernels without it keep exactly the
 // code (and code layout) they have when no caller asks for it.
-template <bool CAUSAL, bool LSE, bool VARLEN>
+template <bool CAUSAL, bool LSE, bool VARLEN, bool DSCALE>
 hipError_t launch_c(const Problem& p) {
     if (p.d_qk == 128)
-        return p.p_mode == 0 ? launch_t<128, 0, CAUSAL, LSE, VARLEN>(p) : launch_t<128, 1, CAUSAL, LSE, VARLEN>(p);
+        return p.p_mode == 0 ? launch_t<128, 0, CAUSAL, LSE, VARLEN, DSCALE>(p)
+                             : launch_t<128, 1, CAUSAL, LSE, VARLEN, DSCALE>(p);
     if (p.d_qk == 192)
-        return p.p_mode == 0 ? launch_t<192, 0, CAUSAL, LSE, VARLEN>(p) : launch_t<192, 1, CAUSAL, LSE, VARLEN>(p);
+        return p.p_mode == 0 ? launch_t<192, 0, CAUSAL, LSE, VARLEN, DSCALE>(p)
+                             : launch_t<192, 1, CAUSAL, LSE, VARLEN, DSCALE>(p);
     return hipErrorInvalidValue;
 }
 
-template <bool VARLEN>
+// Scales in device memory are a template switch too (equal-length calls only), so
+// the kernels that take them by value keep their code.
+template <bool VARLEN, bool DSCALE>
 hipError_t launch_v(const Problem& p) {
-    if (p.lse) return p.causal ? launch_c<true, true, VARLEN>(p) : launch_c<false, true, VARLEN>(p);
-    return p.causal ? launch_c<true, false, VARLEN>(p) : launch_c<false, false, VARLEN>(p);
+    if (p.lse) return p.causal ? launch_c<true, true, VARLEN, DSCALE>(p) : launch_c<false, true, VARLEN, DSCALE>(p);
+    return p.causal ? launch_c<true, false, VARLEN, DSCALE>(p) : launch_c<false, false, VARLEN, DSCALE>(p);
 }
 
 }  // namespace
 
-hipError_t launch_fp8(const Problem& p) { return p.cu ? launch_v<true>(p) : launch_v<false>(p); }
+hipError_t launch_fp8(const Problem& p) {
+    if (p.cu) return p.dq ? hipErrorInvalidValue : launch_v<true, false>(p);
+    return p.dq ? launch_v<false, true>(p) : launch_v<false, false>(p);
+}
 
 }  // namespace attnfwd

@@ -27,6 +27,11 @@ struct Problem {
     int total;
     const int* cu_k;
     int total_k;
+    // FP8 only: per-tensor scales in device memory (one float each), or null (use the
+    // values above)
+    const float* dq;
+    const float* dk;
+    const float* dv;
 };
 
 hipError_t launch_fp8(const Problem& p);

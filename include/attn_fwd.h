@@ -117,6 +117,26 @@ int attn_fwd_fp8_lse(const void* q, const void* k, const void* v, void* o, float
                      int causal, int p_mode, hipStream_t stream);
 
 /*
+ * attn_fwd_fp8_lse with the per-tensor scales read from device memory, so that a
+ * call can follow attn_rotate_quant_bf16 (which writes Q's and K's scales to
+ * device memory) on the same stream with no host synchronisation in between.
+ *
+ * q_scale, k_scale, v_scale: device pointers to one float each, 4-byte aligned,
+ *      read by the kernel when it runs (values as for attn_fwd_fp8: finite and
+ *      > 0; they cannot be checked on the host - other values give undefined
+ *      outputs, never an out-of-bounds access).  The kernel forms
+ *      q_scale * k_scale * softmax_scale * log2(e) in double precision as the
+ *      host does for attn_fwd_fp8, so both entry points give the same bits.
+ * lse: NULL or as for attn_fwd_fp8_lse.  Other arguments, behaviour and errors
+ *      as attn_fwd_fp8_lse; a null or misaligned scale pointer is
+ *      ATTN_E_INVALID_ARG.
+ */
+int attn_fwd_fp8_dscale(const void* q, const void* k, const void* v, void* o, float* lse,
+                        const float* q_scale, const float* k_scale, const float* v_scale, float softmax_scale,
+                        int B, int Hq, int Hkv, int S, int d_qk, int d_v, int causal, int p_mode,
+                        hipStream_t stream);
+
+/*
  * BF16 causal prefill attention (the BF16 kernel of "Zyphra ZYFA: FP8
  * FlashAttention...", section "What is ZYFA?").
  *

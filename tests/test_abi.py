@@ -33,10 +33,11 @@ def declared_functions():
 
 def test_exports_every_declared_symbol(lib):
     decl = declared_functions()
-    assert {"attn_fwd_fp8", "attn_fwd_fp8_lse", "attn_fwd_fp8_varlen", "attn_fwd_bf16", "attn_fwd_bf16_lse",
+    assert {"attn_fwd_fp8", "attn_fwd_fp8_lse", "attn_fwd_fp8_varlen", "attn_fwd_fp8_dscale", "attn_fwd_bf16",
+            "attn_fwd_bf16_lse",
             "attn_fwd_bf16_varlen", "attn_last_error", "attn_abi_version"} <= decl
     assert decl <= binding.exported_symbols()
-    assert lib.attn_abi_version() == 103
+    assert lib.attn_abi_version() == 104
 
 
 # fake, never-dereferenced, 16-byte aligned device addresses of disjoint buffers
@@ -165,6 +166,25 @@ def test_varlen_host_validation(lib, entry, kw, status):
     assert (msg == "") == (status == OK)
     if status != OK:
         assert msg.startswith(f"attn_fwd_{entry}_varlen")
+
+
+SC = 0x70000000
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q_scale=0), INVALID), (dict(v_scale=0), INVALID), (dict(k_scale=SC + 2), INVALID),
+    (dict(d_qk=64), UNSUPPORTED), (dict(p_mode=3), INVALID), (dict(o=Q + 64), INVALID),
+    (dict(S=0, q=0, k=0, v=0, o=0), OK),
+])
+def test_dscale_host_validation(lib, kw, status):
+    a = dict(q=Q, k=K, v=V, o=O, lse=0, q_scale=SC, k_scale=SC + 4, v_scale=SC + 8, softmax_scale=0.0,
+             B=1, Hq=4, Hkv=2, S=128, d_qk=128, d_v=128, causal=1, p_mode=1)
+    a.update(kw)
+    assert binding.attn_fwd_fp8_dscale_raw(**a) == status
+    msg = binding.attn_last_error()
+    assert (msg == "") == (status == OK)
+    if status != OK:
+        assert msg.startswith("attn_fwd_fp8_dscale")
 
 
 def rotq(**kw):

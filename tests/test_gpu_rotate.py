@@ -142,3 +142,26 @@ def test_rotation_cuts_end_to_end_error_with_outlier_channels(mode):
     e_rot = rel_rms(attend(rq, float(rqs.item()), rk, float(rks.item())), ref)
     print(f"[parity] rotation end to end ({mode}): rel-RMS {e_plain:.4f} -> {e_rot:.4f}")
     assert e_rot < 0.5 * e_plain
+
+
+@pytest.mark.parametrize("mode", ["lean", "exact"])
+@pytest.mark.parametrize("dqk", [128, 192])
+def test_rotation_then_attention_with_device_scales(mode, dqk):
+    # rotate Q and K, then attend with the scales the rotation wrote, all on one stream with no
+    # host synchronisation; byte-identical to the call taking the same scales by value
+    w = W.Workload("chain", 1, 4, 2, 777, dqk, 128)
+    d = W.make_bf16(w, seed=23)
+    dev = "cuda:0"
+    q, k = d["q"].to(dev), d["k"].to(dev)
+    v8, vs = W.quantize_e4m3(d["v"].float())
+    v8 = v8.to(dev)
+    q8, qs = binding.rotate_quant_bf16(q)
+    k8, ks = binding.rotate_quant_bf16(k)
+    vs_dev = torch.tensor([vs], dtype=torch.float32, device=dev)
+    out_dev, lse_dev = binding.attn_fwd_fp8(q8, k8, v8, qs, ks, vs_dev, p_mode=mode, return_lse=True)
+    torch.cuda.synchronize()
+    out_val, lse_val = binding.attn_fwd_fp8(q8, k8, v8, float(qs.item()), float(ks.item()), vs, p_mode=mode,
+                                            return_lse=True)
+    torch.cuda.synchronize()
+    assert torch.equal(out_dev.view(torch.int16), out_val.view(torch.int16))
+    assert torch.equal(lse_dev, lse_val)
