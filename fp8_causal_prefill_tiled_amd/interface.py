@@ -44,6 +44,24 @@ def _(q8, k8, v8, q_scale, k_scale, v_scale, softmax_scale, causal, p_mode, with
     return _fake_outputs(q8, v8, with_lse)
 
 
+@torch.library.custom_op(f"{_OPS}::attn_fwd_fp8_dscale", mutates_args=(), device_types="cuda")
+def _attn_fwd_fp8_dscale_op(q8: torch.Tensor, k8: torch.Tensor, v8: torch.Tensor, q_scale: torch.Tensor,
+                            k_scale: torch.Tensor, v_scale: torch.Tensor, softmax_scale: float, causal: bool,
+                            p_mode: int, with_lse: bool) -> tuple[torch.Tensor, torch.Tensor]:
+    sm = softmax_scale if softmax_scale > 0 else None
+    if not with_lse:
+        out = binding.attn_fwd_fp8(q8, k8, v8, q_scale, k_scale, v_scale, softmax_scale=sm, causal=causal,
+                                   p_mode=p_mode)
+        return out, q8.new_empty((0,), dtype=torch.float32)
+    return binding.attn_fwd_fp8(q8, k8, v8, q_scale, k_scale, v_scale, softmax_scale=sm, causal=causal,
+                                p_mode=p_mode, return_lse=True)
+
+
+@_attn_fwd_fp8_dscale_op.register_fake
+def _(q8, k8, v8, q_scale, k_scale, v_scale, softmax_scale, causal, p_mode, with_lse):
+    return _fake_outputs(q8, v8, with_lse)
+
+
 @torch.library.custom_op(f"{_OPS}::attn_fwd_bf16", mutates_args=(), device_types="cuda")
 def _attn_fwd_bf16_op(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, softmax_scale: float, causal: bool,
                       with_lse: bool) -> tuple[torch.Tensor, torch.Tensor]:
@@ -115,12 +133,12 @@ def flash_attn_func(q, k, v, dropout_p=0.0, softmax_scale=None, causal=False, wi
     the GPU, equal query and key lengths.  bfloat16 inputs run the BF16 kernel;
     float8_e4m3fn (or uint8 e4m3 bytes) inputs run the FP8 kernel and need the
     per-tensor scales ``q_descale``/``k_descale``/``v_descale`` (float or
-    one-element tensor: dequantised value = descale * code), with ``p_mode``
-    "lean" or "exact".  Returns the bf16 output (B, S, Hq, d_v); with
+    one-element tensor: dequantised value = descale * code; GPU tensors for all
+    three are read by the kernel itself, with no host synchronisation), with
+    ``p_mode`` "lean" or "exact".  Returns the bf16 output (B, S, Hq, d_v); with
     ``return_attn_probs`` returns (out, lse, None), lse fp32 (B, Hq, S), as
     flash_attn_func does (its third value, the dropout mask, is always None).
-    Scales given as tensors are read with ``.item()`` (a host sync); pass
-    floats inside ``torch.compile``d code.
+    Scales given as CPU tensors are read with ``.item()``.
 
     Options outside the kernels' scope raise NotImplementedError: dropout,
     sliding windows, softcapping and ALiBi.  ``deterministic`` is accepted and
@@ -139,9 +157,15 @@ def flash_attn_func(q, k, v, dropout_p=0.0, softmax_scale=None, causal=False, wi
         if k.dtype not in _FP8_DTYPES or v.dtype not in _FP8_DTYPES:
             raise TypeError("q, k and v must all be FP8 e4m3 (or all bfloat16)")
         q8, k8, v8 = (t.view(torch.uint8) if t.dtype != torch.uint8 else t for t in (q, k, v))
-        out, lse = _attn_fwd_fp8_op(q8, k8, v8, _scale(q_descale, "q_descale"), _scale(k_descale, "k_descale"),
-                                    _scale(v_descale, "v_descale"), sm, bool(causal),
-                                    int(binding._P_MODES[p_mode]), bool(return_attn_probs))
+        scales = (q_descale, k_descale, v_descale)
+        if all(isinstance(x, torch.Tensor) and x.is_cuda for x in scales):
+            # scales in device memory: read by the kernel, no host synchronisation
+            out, lse = _attn_fwd_fp8_dscale_op(q8, k8, v8, *(x.reshape(1).float() for x in scales), sm, bool(causal),
+                                               int(binding._P_MODES[p_mode]), bool(return_attn_probs))
+        else:
+            out, lse = _attn_fwd_fp8_op(q8, k8, v8, _scale(q_descale, "q_descale"), _scale(k_descale, "k_descale"),
+                                        _scale(v_descale, "v_descale"), sm, bool(causal),
+                                        int(binding._P_MODES[p_mode]), bool(return_attn_probs))
     elif q.dtype == torch.bfloat16:
         if k.dtype != torch.bfloat16 or v.dtype != torch.bfloat16:
             raise TypeError("q, k and v must all be bfloat16 (or all FP8 e4m3)")

@@ -117,3 +117,20 @@ def test_varlen_opcheck_and_compile():
     compiled = torch.compile(f, backend="aot_eager", fullgraph=True)(q, k, cq, ck)
     torch.cuda.synchronize()
     assert torch.equal(eager, compiled)
+
+
+def test_fp8_wrapper_device_scales_match_and_compile():
+    d, q8, k8, v8 = _fp8(S=333)
+    qf, kf, vf = (t.view(torch.float8_e4m3fn) for t in (q8, k8, v8))
+    ds = [torch.tensor([d[n]], dtype=torch.float32, device=DEV) for n in ("q_scale", "k_scale", "v_scale")]
+    ref = flash_attn_func(qf, kf, vf, causal=True, q_descale=d["q_scale"], k_descale=d["k_scale"],
+                          v_descale=d["v_scale"])
+
+    def f(q, k, v, a, b, c):
+        return flash_attn_func(q, k, v, causal=True, q_descale=a, k_descale=b, v_descale=c)
+
+    out = f(qf, kf, vf, *ds)
+    comp = torch.compile(f, backend="aot_eager", fullgraph=True)(qf, kf, vf, *ds)
+    torch.cuda.synchronize()
+    assert torch.equal(out.view(torch.int16), ref.view(torch.int16))
+    assert torch.equal(comp.view(torch.int16), ref.view(torch.int16))
