@@ -20,7 +20,8 @@ P_EXACT, P_LEAN = 0, 1
 _P_MODES = {"exact": P_EXACT, "lean": P_LEAN, P_EXACT: P_EXACT, P_LEAN: P_LEAN}
 
 _EXPORTS = ("attn_fwd_fp8", "attn_fwd_fp8_lse", "attn_fwd_fp8_varlen", "attn_fwd_fp8_dscale", "attn_fwd_bf16", "attn_fwd_bf16_lse",
-            "attn_fwd_bf16_varlen", "attn_rotate_quant_bf16", "attn_last_error", "attn_abi_version")
+            "attn_fwd_bf16_varlen", "attn_rotate_quant_bf16", "attn_rotate_quant_bf16_prescaled", "attn_last_error",
+            "attn_abi_version")
 
 
 class AttnError(RuntimeError):
@@ -61,6 +62,8 @@ def load_library():
     lib.attn_fwd_bf16_varlen.restype = i
     lib.attn_rotate_quant_bf16.argtypes = [vp, vp, vp, i, i, i, i, vp]
     lib.attn_rotate_quant_bf16.restype = i
+    lib.attn_rotate_quant_bf16_prescaled.argtypes = [vp, vp, vp, vp, i, i, i, i, vp]
+    lib.attn_rotate_quant_bf16_prescaled.restype = i
     lib.attn_last_error.argtypes = []
     lib.attn_last_error.restype = ctypes.c_char_p
     lib.attn_abi_version.argtypes = []
@@ -161,6 +164,31 @@ def rotate_quant_bf16(x, out=None, scale=None, stream=None):
     _check(load_library().attn_rotate_quant_bf16(x.data_ptr(), out.data_ptr(), scale.data_ptr(), B, S, H, d,
                                                  _stream_ptr(stream, x.device)))
     return out, scale
+
+
+def attn_rotate_quant_bf16_prescaled_raw(x, x8, scale, amax, B, S, H, d, stream=0):
+    return load_library().attn_rotate_quant_bf16_prescaled(x, x8, scale, amax, B, S, H, d, stream)
+
+
+def rotate_quant_bf16_prescaled(x, scale, out=None, with_amax=True, stream=None):
+    """One-pass Hadamard rotation + e4m3 quantisation of a bf16 (B,S,H,d) Q or K tensor with a
+    scale known in advance (one-element float32 GPU tensor).  Returns (codes, amax) where amax
+    is a one-element float32 GPU tensor holding max |rotated| (None if not with_amax)."""
+    B, S, H, d = _bshd(x, "x")
+    if x.dtype != torch.bfloat16:
+        raise TypeError(f"x must be bfloat16, got {x.dtype}")
+    if not (isinstance(scale, torch.Tensor) and scale.is_cuda and scale.dtype == torch.float32
+            and scale.numel() == 1):
+        raise ValueError("scale must be a one-element float32 GPU tensor")
+    if out is None:
+        out = torch.empty(x.shape, dtype=torch.uint8, device=x.device)
+    elif out.shape != x.shape or out.dtype != torch.uint8 or not out.is_contiguous():
+        raise ValueError("out must be a contiguous uint8 tensor of x's shape")
+    amax = torch.empty(1, dtype=torch.float32, device=x.device) if with_amax else None
+    _check(load_library().attn_rotate_quant_bf16_prescaled(x.data_ptr(), out.data_ptr(), scale.data_ptr(),
+                                                           0 if amax is None else amax.data_ptr(), B, S, H, d,
+                                                           _stream_ptr(stream, x.device)))
+    return out, amax
 
 
 def _lse_out(return_lse, B, Hq, S, device):

@@ -220,8 +220,30 @@ int attn_rotate_quant_bf16(const void* x, void* x8, float* scale, int B, int S, 
     return finish(attnfwd::launch_rotate_quant(x, x8, scale, n_el, d, stream), who);
 }
 
+int attn_rotate_quant_bf16_prescaled(const void* x, void* x8, const float* scale, float* amax, int B, int S, int H,
+                                     int d, hipStream_t stream) {
+    const char* who = "attn_rotate_quant_bf16_prescaled";
+    if (B < 0 || S < 0 || H <= 0) return fail(ATTN_E_INVALID_ARG, "%s: B=%d S=%d H=%d out of range", who, B, S, H);
+    if (d != 128 && d != 192) return fail(ATTN_E_UNSUPPORTED, "%s: d=%d unsupported (128 or 192)", who, d);
+    if (!scale) return fail(ATTN_E_INVALID_ARG, "%s: null scale pointer", who);
+    if ((reinterpret_cast<uintptr_t>(scale) & 3u) != 0 || (reinterpret_cast<uintptr_t>(amax) & 3u) != 0)
+        return fail(ATTN_E_INVALID_ARG, "%s: scale and amax pointers must be 4-byte aligned", who);
+    const int64_t n_el = (int64_t)B * S * H * d;
+    if (n_el * 2 > ((int64_t)1 << 31)) return fail(ATTN_E_UNSUPPORTED, "%s: tensor of %lld elements too large", who, (long long)n_el);
+    if (n_el > 0) {
+        if (!x || !x8) return fail(ATTN_E_INVALID_ARG, "%s: null tensor pointer", who);
+        if (!aligned16(x) || !aligned16(x8)) return fail(ATTN_E_INVALID_ARG, "%s: tensor pointers must be 16-byte aligned", who);
+        if (overlaps(x8, (size_t)n_el, x, (size_t)n_el * 2) ||
+            (amax && (overlaps(amax, 4, x, (size_t)n_el * 2) || overlaps(amax, 4, x8, (size_t)n_el) ||
+                      overlaps(amax, 4, scale, 4))))
+            return fail(ATTN_E_INVALID_ARG, "%s: output overlaps an input", who);
+    }
+    if (n_el == 0 && !amax) { g_err[0] = 0; return ATTN_OK; }   // nothing to write: no HIP call
+    return finish(attnfwd::launch_rotate_quant_prescaled(x, x8, scale, amax, n_el, d, stream), who);
+}
+
 const char* attn_last_error(void) { return g_err; }
 
-int attn_abi_version(void) { return 104; }
+int attn_abi_version(void) { return 105; }
 
 }  // extern "C"

@@ -39,5 +39,8 @@ hipError_t launch_bf16(const Problem& p);
 // Hadamard rotation + per-tensor e4m3 quantisation of n_el bf16 values (rows of
 // d elements); scale points to one device float.
 hipError_t launch_rotate_quant(const void* x, void* x8, float* scale, int64_t n_el, int d, hipStream_t s);
+// The same with the caller's scale (one pass); amax (nullable) receives max |rotated|.
+hipError_t launch_rotate_quant_prescaled(const void* x, void* x8, const float* scale, float* amax, int64_t n_el,
+                                         int d, hipStream_t s);
 
 }  // namespace attnfwd

@@ -127,6 +127,26 @@ constexpr float inv_sqrt_nb() {
 
 __global__ void rq_init(unsigned* cell) { *cell = 0u; }
 
+// Max over the workgroup of the per-thread maxima m of |y| (unnormalised), scaled to
+// the normalised rotation (a positive constant commutes with the maximum, rounding
+// included), folded into *cell by an atomic max on the float's bits (order-
+// preserving for non-negative floats), skipped when the cell already holds more.
+template <int NB>
+__device__ __forceinline__ void commit_max(float m, int lane, unsigned* cell) {
+    m *= inv_sqrt_nb<NB>();
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
+    __shared__ float wmax[kThreads / 64];
+    if (lane == 0) wmax[threadIdx.x >> 6] = m;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+#pragma unroll
+        for (int i = 1; i < kThreads / 64; ++i) m = fmaxf(m, wmax[i]);
+        if (__float_as_uint(m) > __hip_atomic_load(cell, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT))
+            atomicMax(cell, __float_as_uint(m));
+    }
+}
+
 // The max pass runs a fixed grid of grid-stride workgroups: each wave loops over
 // steps of U units of 32 blocks, and each workgroup ends with one reduction and
 // at most one atomic (device-scope operations on one address, served beyond the
@@ -157,28 +177,18 @@ __global__ void __launch_bounds__(kThreads) rq_amax(const __bf16* __restrict__ x
         }
         wave_lds_sync();
     }
-    // max |y| of the normalised rotation: scaling by a positive constant commutes
-    // with the maximum, rounding included
-    m *= inv_sqrt_nb<NB>();
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
-    __shared__ float wmax[kThreads / 64];
-    if (lane == 0) wmax[threadIdx.x >> 6] = m;
-    __syncthreads();
-    if (threadIdx.x == 0) {
-#pragma unroll
-        for (int i = 1; i < kThreads / 64; ++i) m = fmaxf(m, wmax[i]);
-        // the running maximum is usually larger already: read it and skip the atomic
-        if (__float_as_uint(m) > __hip_atomic_load(cell, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT))
-            atomicMax(cell, __float_as_uint(m));
-    }
+    commit_max<NB>(m, lane, cell);
 }
 
 __device__ __forceinline__ float scale_of(float amax) { return amax > 0.0f ? amax / kE4M3Max : 1.0f; }
 
-template <int NB>
+// PRESCALED: quantise with the caller's scale (*scale) instead of the amax cell of
+// the max pass, and, when amax_out is given, fold this tensor's max |y| into it (one
+// pass: the scale comes from an earlier step, the maximum is for the next one).
+template <int NB, bool PRESCALED>
 __global__ void __launch_bounds__(kThreads) rq_quant(const __bf16* __restrict__ x, int64_t nblocks,
-                                                     const unsigned* cell, uint8_t* __restrict__ out) {
+                                                     const unsigned* cell, const float* scale, unsigned* amax_out,
+                                                     uint8_t* __restrict__ out) {
     constexpr int NA = NB / 32;
     // The codes of a unit (32 blocks, contiguous in memory) go through LDS so that the
     // global stores are whole 16-byte chunks: rows of NB + 16 bytes keep the 16-byte
@@ -200,7 +210,19 @@ __global__ void __launch_bounds__(kThreads) rq_quant(const __bf16* __restrict__ 
     wave_lds_sync();
     // one multiply per element by 1/(sqrt(n) scale): within an ulp of dividing the
     // normalised value by the scale, so the rounding to e4m3 can differ only at ties
-    const float f = inv_sqrt_nb<NB>() / scale_of(__uint_as_float(*cell));
+    const float f = inv_sqrt_nb<NB>() / (PRESCALED ? *scale : scale_of(__uint_as_float(*cell)));
+    if constexpr (PRESCALED) {
+        if (amax_out != nullptr) {   // uniform: the same pointer in every thread
+            float m = 0.0f;
+#pragma unroll
+            for (int u = 0; u < U; ++u)
+#pragma unroll
+                for (int a = 0; a < NA; ++a)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) m = fmaxf(m, fabsf(y[u][a][r]));
+            commit_max<NB>(m, lane, amax_out);
+        }
+    }
 #pragma unroll
     for (int u = 0; u < U; ++u) {
         // accumulators 4g..4g+3 of chunk a: columns 32a + 8g + 4(lane/32) + 0..3 of
@@ -245,13 +267,39 @@ hipError_t launch_t(const __bf16* x, uint8_t* x8, unsigned* cell, int64_t n_el, 
         if (grid > 0x7fffffffLL) return hipErrorInvalidConfiguration;
         const unsigned agrid = (unsigned)(grid < kAmaxGrid ? grid : kAmaxGrid);
         hipLaunchKernelGGL((rq_amax<NB>), dim3(agrid), dim3(kThreads), 0, s, x, nblocks, cell);
-        hipLaunchKernelGGL((rq_quant<NB>), dim3((unsigned)grid), dim3(kThreads), 0, s, x, nblocks, cell, x8);
+        hipLaunchKernelGGL((rq_quant<NB, false>), dim3((unsigned)grid), dim3(kThreads), 0, s, x, nblocks, cell,
+                           nullptr, nullptr, x8);
     }
     hipLaunchKernelGGL(rq_finish, dim3(1), dim3(1), 0, s, cell);
     return hipGetLastError();
 }
 
+template <int NB>
+hipError_t launch_pre_t(const __bf16* x, uint8_t* x8, const float* scale, unsigned* amax, int64_t n_el,
+                        hipStream_t s) {
+    const int64_t nblocks = n_el / NB;
+    constexpr int64_t per_wg = (int64_t)32 * U * (kThreads / 64);
+    if (amax) hipLaunchKernelGGL(rq_init, dim3(1), dim3(1), 0, s, amax);
+    if (nblocks > 0) {
+        const int64_t grid = (nblocks + per_wg - 1) / per_wg;
+        if (grid > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+        hipLaunchKernelGGL((rq_quant<NB, true>), dim3((unsigned)grid), dim3(kThreads), 0, s, x, nblocks, nullptr,
+                           scale, amax, x8);
+    }
+    return hipGetLastError();
+}
+
 }  // namespace
+
+hipError_t launch_rotate_quant_prescaled(const void* x, void* x8, const float* scale, float* amax, int64_t n_el,
+                                         int d, hipStream_t s) {
+    auto* cell = reinterpret_cast<unsigned*>(amax);
+    if (d % 128 == 0)
+        return launch_pre_t<128>(static_cast<const __bf16*>(x), static_cast<uint8_t*>(x8), scale, cell, n_el, s);
+    if (d % 64 == 0)
+        return launch_pre_t<64>(static_cast<const __bf16*>(x), static_cast<uint8_t*>(x8), scale, cell, n_el, s);
+    return hipErrorInvalidValue;
+}
 
 hipError_t launch_rotate_quant(const void* x, void* x8, float* scale, int64_t n_el, int d, hipStream_t s) {
     auto* cell = reinterpret_cast<unsigned*>(scale);

@@ -226,6 +226,22 @@ int attn_fwd_bf16_varlen(const void* q, const void* k, const void* v, void* o, f
                          int total_q, int total_k, float softmax_scale, int Hq, int Hkv, int d_qk, int d_v,
                          int causal, hipStream_t stream);
 
+/*
+ * One-pass form of attn_rotate_quant_bf16 for a scale known in advance (for
+ * example from the previous step or a calibration run; per-tensor "delayed"
+ * scaling): the same rotation, codes e4m3 RNE(rotated / *scale) saturating at
+ * +-448, and, when amax is not NULL, *amax = max |rotated| of this tensor (the
+ * next call's scale is amax / 448).  One streaming pass instead of two.
+ *
+ * scale: device pointer to one float (> 0 and finite; not checkable on the host),
+ *        read by the kernel.  amax: device pointer to one float, or NULL.  Both
+ *        4-byte aligned, amax not overlapping x, x8 or scale.  Other arguments,
+ *        behaviour and errors as attn_rotate_quant_bf16.  Enqueues one kernel (two
+ *        with amax); allocates nothing.
+ */
+int attn_rotate_quant_bf16_prescaled(const void* x, void* x8, const float* scale, float* amax, int B, int S, int H,
+                                     int d, hipStream_t stream);
+
 /* Message for the calling thread's last non-OK status ("" if none).  The
  * returned storage is thread-local and valid until that thread's next call. */
 const char* attn_last_error(void);

@@ -37,7 +37,7 @@ def test_exports_every_declared_symbol(lib):
             "attn_fwd_bf16_lse",
             "attn_fwd_bf16_varlen", "attn_last_error", "attn_abi_version"} <= decl
     assert decl <= binding.exported_symbols()
-    assert lib.attn_abi_version() == 104
+    assert lib.attn_abi_version() == 105
 
 
 # fake, never-dereferenced, 16-byte aligned device addresses of disjoint buffers
@@ -185,6 +185,22 @@ def test_dscale_host_validation(lib, kw, status):
     assert (msg == "") == (status == OK)
     if status != OK:
         assert msg.startswith("attn_fwd_fp8_dscale")
+
+
+def rotp(**kw):
+    a = dict(x=Q, x8=K, scale=V, amax=O, B=1, S=64, H=2, d=128)
+    a.update(kw)
+    return binding.attn_rotate_quant_bf16_prescaled_raw(**a)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(scale=0), INVALID), (dict(amax=O + 2), INVALID), (dict(scale=V + 1), INVALID),
+    (dict(d=96), UNSUPPORTED), (dict(x=0), INVALID), (dict(amax=Q + 64), INVALID),
+    (dict(x8=Q + 4096), INVALID), (dict(B=0, x=0, x8=0, amax=0), OK),   # empty, no amax: nothing launched
+])
+def test_rotate_quant_prescaled_validation(lib, kw, status):
+    assert rotp(**kw) == status
+    assert (binding.attn_last_error() == "") == (status == OK)
 
 
 def rotq(**kw):

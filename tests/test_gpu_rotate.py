@@ -165,3 +165,23 @@ def test_rotation_then_attention_with_device_scales(mode, dqk):
     torch.cuda.synchronize()
     assert torch.equal(out_dev.view(torch.int16), out_val.view(torch.int16))
     assert torch.equal(lse_dev, lse_val)
+
+
+@pytest.mark.parametrize("dqk", [128, 192])
+def test_prescaled_one_pass_matches_two_pass(dqk):
+    # with the two-pass scale, the one-pass form writes the same codes, and its amax / 448 is that
+    # scale (the same maximum of the same rotated values)
+    w = W.Workload("pre", 2, 3, 3, 301, dqk, 128)
+    x = W.make_bf16(w, seed=41)["q"].to("cuda:0")
+    codes, scale = binding.rotate_quant_bf16(x)
+    codes2, amax = binding.rotate_quant_bf16_prescaled(x, scale)
+    torch.cuda.synchronize()
+    assert torch.equal(codes, codes2)
+    assert np.float32(amax.item()) / np.float32(E4M3_MAX) == np.float32(scale.item())
+    # a different scale gives the oracle's codes for that scale (up to fp32 ties)
+    s2 = torch.tensor([scale.item() * 1.37], dtype=torch.float32, device="cuda:0")
+    codes3, _ = binding.rotate_quant_bf16_prescaled(x, s2, with_amax=False)
+    torch.cuda.synchronize()
+    r = rotate(x.float().cpu().numpy().astype(np.float64))
+    exp = encode_e4m3_rne(np.clip(r / np.float64(np.float32(s2.item())), -E4M3_MAX, E4M3_MAX))
+    assert np.mean(codes3.cpu().numpy() == exp) > 0.999
