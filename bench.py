@@ -20,6 +20,7 @@ if ROOT not in sys.path:
 METRIC = "causal prefill attention TFLOP/s & % FP8 peak (d=128, S=32K); RMS err vs fp64"
 # MI355X published dense peaks, TFLOP/s
 PEAK_TFLOPS = {"fp8": 5000.0, "bf16": 2500.0}
+PEAK_SCLK_MHZ = 2400.0          # the shader clock those peaks assume
 # The pages' own figure for this workload (ZYFA, FP8, d=128, 32K tokens, Gaussian inputs, MI355X)
 PAGES_TFLOPS = {("gauss32k", "fp8"): 2672.0}
 
@@ -442,6 +443,10 @@ def main():
             "frac_of_peak": flops / (avg_ms * 1e-3) / 1e12 / peak,
             "energy": sampler.summary(flops * args.steps, wall),
         }
+        # the same fraction against the dense peak scaled to the sampled DPM clock (peak at 2.4 GHz)
+        mhz = paths[mode]["energy"].get("sclk_mhz_avg")
+        paths[mode]["frac_of_peak_at_sampled_sclk"] = (
+            paths[mode]["frac_of_peak"] * PEAK_SCLK_MHZ / mhz if mhz else None)
     clk_after = sclk_mhz()
     study = None
     if args.input_study and args.dtype == "fp8":
