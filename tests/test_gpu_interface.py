@@ -7,7 +7,8 @@ import torch
 
 from fp8_causal_prefill_tiled_amd import binding
 from fp8_causal_prefill_tiled_amd import workloads as W
-from fp8_causal_prefill_tiled_amd.interface import flash_attn_func, _attn_fwd_bf16_op, _attn_fwd_fp8_op
+from fp8_causal_prefill_tiled_amd.interface import (flash_attn_func, _attn_fwd_bf16_op, _attn_fwd_fp8_dscale_op,
+                                                    _attn_fwd_fp8_op)
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
@@ -134,3 +135,4 @@ def test_fp8_wrapper_device_scales_match_and_compile():
     torch.cuda.synchronize()
     assert torch.equal(out.view(torch.int16), ref.view(torch.int16))
     assert torch.equal(comp.view(torch.int16), ref.view(torch.int16))
+    torch.library.opcheck(_attn_fwd_fp8_dscale_op, (q8, k8, v8, *ds, 0.0, True, 1, True))
