@@ -120,3 +120,37 @@ def sample_rows(S, n, seed=BASE_SEED + 7):
     perm = torch.randperm(S, generator=_gen(seed))[:n]
     rows = sorted(fixed | set(int(r) for r in perm[: max(0, n - len(fixed))]))
     return torch.tensor(rows, dtype=torch.int64)
+
+
+def sample_rows_long(S, n, seed=BASE_SEED + 11):
+    """A seeded sorted sample of about n distinct query rows weighted towards long causal rows:
+    rows 0, 1, 63, 64 and S-1, then n/8 rows drawn uniformly from 0..S-1 and the rest from
+    the second half S/2..S-1 (where almost all of a causal launch's work is)."""
+    if n >= S:
+        return torch.arange(S)
+    fixed = {r for r in (0, 1, 63, 64, S - 1) if 0 <= r < S}
+    g = _gen(seed)
+    spread = torch.randperm(S, generator=g)[: max(1, n // 8)]
+    half = S // 2
+    late = half + torch.randperm(S - half, generator=g)
+    rows = fixed | set(int(r) for r in spread)
+    for r in late.tolist():
+        if len(rows) >= n:
+            break
+        rows.add(int(r))
+    return torch.tensor(sorted(rows), dtype=torch.int64)
+
+
+def sample_rows_strata(S, n_first=256, n_rest=1024, seed=BASE_SEED + 13):
+    """Rows for estimating a whole-tensor sum over query rows: every row below n_first, plus a
+    seeded uniform sample of n_rest rows from n_first..S-1.  Returns (rows, weights): the weight
+    of a row is the number of rows it stands for (1 for the first stratum)."""
+    first = torch.arange(min(n_first, S))
+    if S <= n_first + n_rest:
+        return torch.arange(S), torch.ones(S, dtype=torch.float64)
+    rest = n_first + torch.randperm(S - n_first, generator=_gen(seed))[:n_rest]
+    rest = torch.sort(rest).values
+    rows = torch.cat([first, rest])
+    weights = torch.cat([torch.ones(len(first), dtype=torch.float64),
+                         torch.full((n_rest,), (S - n_first) / n_rest, dtype=torch.float64)])
+    return rows, weights

@@ -43,6 +43,16 @@ in their order, in fp64 except where the method itself rounds:
 ``rounding=False`` (exact path only) skips the e4m3 rounding in step 4; the
 result is then the plain definition, which pins this module to
 ``attention64`` (tests/test_oracle_emulate.py).
+
+Rounding decisions near a boundary.  Step 4 turns a real number into an integer
+code, so a score that lies very close to a rounding boundary has two valid
+codes: the pages fix neither the precision of the scores nor the order of the
+matrix instruction's sums.  ``rounding_alternatives`` lists, for one query row,
+every key whose code changes when its log2-domain score moves by at most
+eps_j = kappa * c * sum_m max_{k in step m} |q_k k_jk| (an error scale of a dot
+product summed in steps of 64 products, each step accurate to a fraction of its
+largest product), and the code it would take then.  Reading: a result that differs from the
+emulation only by such alternative codes is as correct as the emulation.
 """
 import numpy as np
 
@@ -174,3 +184,67 @@ def encode_probability_lean(y):
 def encode_probability_exact(y):
     """Exact-path code for y: e4m3_RNE(2^y)."""
     return encode_e4m3_rne(np.exp2(np.asarray(y, dtype=np.float64)))
+
+
+def rounding_alternatives(q8, k8, v8, q_scale, k_scale, v_scale, sm_scale=None, p_mode="exact", b=0, i=0, h=0,
+                          causal=True, kappa=2.0 ** -10):
+    """One query row of the emulation together with its ambiguous rounding decisions.
+
+    Returns a dict with
+      ``out``    O_i (d_v,), as emulate_fp8 returns it;
+      ``vhat``   the dequantised value rows of the visible keys (n, d_v);
+      ``weight`` W_j = p~_j * 2^(M_b(j) - R_i) of every visible key (n,), so that
+                 O_i = sum_j W_j vhat_j / sum_j W_j (steps 3-6);
+      ``alt``    a list of (j, W_alt): keys whose code differs when the log2-domain score
+                 t_j moves anywhere within [t_j - eps_j, t_j + eps_j] (block exponents held
+                 fixed), with the weight each other code gives.
+    eps_j = kappa * c * sum_m max_{k in [64m, 64m+64)} |decode(Q8[i,k]) * decode(K8[j,k])| in
+    log2 units (c = the log2-domain score factor).  kappa = 0 lists nothing.
+    """
+    q8 = np.asarray(q8, dtype=np.uint8)
+    k8 = np.asarray(k8, dtype=np.uint8)
+    v8 = np.asarray(v8, dtype=np.uint8)
+    B, S, Hq, dqk = q8.shape
+    Sk, Hkv = k8.shape[1], k8.shape[2]
+    sm = 1.0 / np.sqrt(dqk) if sm_scale is None else float(sm_scale)
+    C = float(q_scale) * float(k_scale) * sm * LOG2E
+    A = np.float64(np.float32(8.0 * C))
+    g = kv_head(h, Hq, Hkv)
+    n = int(visible_keys(np.array([i]), S, Sk, causal)[0])
+    if n == 0:
+        return {"out": np.zeros(v8.shape[3]), "vhat": np.zeros((0, v8.shape[3])), "weight": np.zeros(0), "alt": []}
+    nb = (n + BLOCK_KEYS - 1) // BLOCK_KEYS
+    npad = nb * BLOCK_KEYS
+    qd = decode_e4m3(q8[b, i, h, :])
+    kd = decode_e4m3(k8[b, :n, g, :])
+    s = np.zeros(npad)
+    s[:n] = kd @ qd
+    sabs = np.zeros(npad)
+    prod = np.abs(kd * qd[None, :])
+    for m0 in range(0, dqk, 64):
+        sabs[:n] += prod[:, m0:m0 + 64].max(axis=1)
+    valid = (np.arange(npad) < n).reshape(1, nb, BLOCK_KEYS)
+    s3 = s.reshape(1, nb, BLOCK_KEYS)
+    p, M, has = _block_probs(s3 * C, valid, p_mode, True, s=s3, A=A)
+    R = np.max(np.where(has, M, -np.inf))
+    fac = np.repeat(np.exp2(M[0] - R), BLOCK_KEYS)[:n]
+    weight = p.reshape(-1)[:n] * fac
+    vhat = float(v_scale) * decode_e4m3(v8[b, :n, g, :])
+    out = weight @ vhat / weight.sum()
+    eps = (kappa * C * sabs[:n])
+    Mk = np.repeat(M[0], BLOCK_KEYS)[:n]
+    t = s[:n] * C
+    cands = []
+    for sign in (-1.0, 1.0):
+        if p_mode == "exact":
+            palt = round_to_e4m3(np.exp2(t + sign * eps - Mk + 8.0))
+        else:
+            code = np.clip(np.rint(A * s[:n] + (120.0 - 8.0 * Mk) + sign * 8.0 * eps), 0, 126)
+            palt = decode_e4m3(code.astype(np.uint8))
+        cands.append(palt)
+    alt = []
+    base = p.reshape(-1)[:n]
+    for j in np.flatnonzero((cands[0] != base) | (cands[1] != base)):
+        for palt in sorted({float(cands[0][j]), float(cands[1][j])} - {float(base[j])}):
+            alt.append((int(j), palt * fac[j]))
+    return {"out": out, "vhat": vhat, "weight": weight, "alt": alt}

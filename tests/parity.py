@@ -16,7 +16,28 @@ than the method itself):
   where e is the emulation's own error vs fp64 - rounding P to e4m3 alone leaves
   1-3% relative RMS on Gaussian values, so the bar is the method's own error
   plus the output rounding.
-* BF16 path vs fp64: <= 4e-3.
+* BF16 path vs fp64: <= 4e-3 over the sample, <= 6e-3 on every row (bf16 output
+  rounding plus bf16 probabilities: ~2.3e-3 per row at the median).
+
+Per-row bars.  A whole-tensor (Frobenius) figure is dominated by the short
+early rows: a causal row that sees n keys has an output norm of order
+sqrt(e/n)*|v|, so rows 0 and 1 alone carry most of the norm of a long
+sequence.  Every FP8 comparison therefore also bounds the error of each row
+against that row's own norm (relative RMS over d_v):
+
+* median over the checked rows of GPU vs emulation: <= 3e-3 (ROW_MEDIAN_EMU),
+  the level of the bf16 output rounding (1.1e-3 to 2.3e-3 per row);
+* every checked row: <= 5e-3 (ROW_BASE) once the rounding decisions that are
+  ambiguous at the matrix instruction's precision are accounted for.  gfx950's
+  FP8 dot products are not correctly rounded fp32 sums (measured: errors up to
+  2^-11.5 of the largest |product| of each 64-product step), so a probability
+  whose score lies that close to an
+  e4m3 rounding boundary has two valid codes, and one such flip in a heavy key
+  moves a long row by up to ~1%.  A row above ROW_BASE passes only if at most
+  MAX_FLIPS of those alternative codes (oracle.emulate.rounding_alternatives,
+  each one step of the code grid) bring it back under ROW_BASE; any other
+  error (a wrong scale, mask, rescale, or a perturbation of the row) cannot be
+  explained that way and fails.
 """
 import numpy as np
 import torch
@@ -24,11 +45,18 @@ import torch
 from fp8_causal_prefill_tiled_amd import binding
 from fp8_causal_prefill_tiled_amd import workloads as W
 from oracle.attention64 import attention_fp64, dequantize, lse_fp64, rel_rms
-from oracle.emulate import emulate_fp8
+from oracle.emulate import emulate_fp8, rounding_alternatives
 from oracle.e4m3 import bf16_rne, decode_e4m3
 
 TOL_EMU = 5e-3
 TOL_BF16 = 4e-3
+ROW_BASE = 5e-3
+TOL_BF16_ROW = 6e-3         # BF16 per row: bf16 output and bf16 P rounding, ~2.3e-3 median
+ROW_MEDIAN_EMU = 3e-3
+MAX_FLIPS = 4
+KAPPA = 2.0 ** -10          # FP8 dot-product error per 64-product step, in units of its largest
+                            # |product| (largest measured on gfx950: 2^-11.5)
+NORTH_STAR_FP8 = 2e-2
 
 
 def tol_fp64(emu_err):
@@ -108,7 +136,90 @@ def row0_expected_fp8(d):
     return bf16_rne(v0 * np.float32(d["v_scale"]))
 
 
-def check_fp8(got, emu, ref, label=""):
+def row_rel_rms(x, ref):
+    """Relative RMS of each output row over d_v: ||x_row - ref_row|| / ||ref_row||, shape (B, rows, heads).
+
+    Rows whose reference is exactly zero (a query that sees no key) give 0 when x is also zero there
+    and +inf otherwise."""
+    x = np.asarray(x, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    num = np.sqrt(np.sum((x - ref) ** 2, axis=-1))
+    den = np.sqrt(np.sum(ref ** 2, axis=-1))
+    with np.errstate(divide="ignore", invalid="ignore"):
+        r = num / den
+    return np.where(den > 0, r, np.where(num > 0, np.inf, 0.0))
+
+
+def explain_by_flips(got_row, info, base=ROW_BASE, max_flips=MAX_FLIPS):
+    """Greedily apply up to ``max_flips`` alternative roundings of one row (``info`` from
+    oracle.emulate.rounding_alternatives) that best explain got_row - O.
+
+    Returns (relative residual after the flips, keys flipped)."""
+    got_row = np.asarray(got_row, dtype=np.float64)
+    W = info["weight"].copy()
+    vhat = info["vhat"]
+    num = W @ vhat
+    den = W.sum()
+    onorm = np.linalg.norm(info["out"])
+    alt = [(j, wa) for j, wa in info["alt"]]
+    used = []
+    r = got_row - num / den
+    for _ in range(max_flips):
+        if np.linalg.norm(r) <= base * onorm or not alt:
+            break
+        js = np.array([j for j, _ in alt])
+        dW = np.array([wa for _, wa in alt]) - W[js]
+        newo = (num[None, :] + dW[:, None] * vhat[js]) / (den + dW)[:, None]
+        resid = np.linalg.norm(got_row[None, :] - newo, axis=1)
+        k = int(np.argmin(resid))
+        if resid[k] >= np.linalg.norm(r):
+            break
+        j = int(js[k])
+        num = num + dW[k] * vhat[j]
+        den = den + dW[k]
+        W[j] += dW[k]
+        used.append(j)
+        r = got_row - newo[k]
+        alt = [(jj, wa) for jj, wa in alt if jj != j]
+    return float(np.linalg.norm(r) / onorm), used
+
+
+def check_rows(got, emu, label="", rows=None, d=None, mode=None, heads=None, causal=True,
+               base=ROW_BASE, median_bound=ROW_MEDIAN_EMU):
+    """Per-row bars of GPU vs the emulation (module docstring).  ``got`` and ``emu`` are
+    (B, rows, heads, d_v); rows above ``base`` are checked against the oracle's alternative
+    roundings (needs the input dict ``d``, ``mode`` and the row and head indices).
+    Returns the per-row errors."""
+    e = row_rel_rms(got, emu)
+    flat = e.reshape(-1)
+    med = float(np.median(flat))
+    rows_idx = np.arange(e.shape[1]) if rows is None else np.asarray(rows)
+    heads_idx = np.arange(e.shape[2]) if heads is None else np.asarray(heads)
+    high = np.argwhere(e > base)
+    explained = []
+    for b, ri, hi in high:
+        where = f"batch {b}, row {rows_idx[ri]}, head {heads_idx[hi]}, error {e[b, ri, hi]:.2e}"
+        if d is None:
+            # several problems concatenated (variable-length batches): the caller checks each
+            # sequence byte for byte against its own equal-length call instead
+            continue
+        info = rounding_alternatives(d["q8"].numpy(), d["k8"].numpy(), d["v8"].numpy(), d["q_scale"],
+                                     d["k_scale"], d["v_scale"], p_mode=mode, b=int(b), i=int(rows_idx[ri]),
+                                     h=int(heads_idx[hi]), causal=causal, kappa=KAPPA)
+        res, used = explain_by_flips(got[b, ri, hi], info, base)
+        assert res <= base, (label, "row not explained by alternative roundings", where, res, used)
+        explained.append((int(rows_idx[ri]), len(used)))
+    print(f"[parity] {label}: per-row vs emulation median {med:.2e}, p99 {np.quantile(flat, 0.99):.2e}, "
+          f"max {flat.max():.2e}, {flat.size} rows; {len(explained)} above {base:.0e} explained by "
+          f"alternative roundings {explained[:6]}")
+    assert med <= median_bound, (label, "median row error", med)
+    return e
+
+
+def check_fp8(got, emu, ref, label="", rows=None, d=None, mode=None, heads=None, causal=True):
+    """Whole-sample and per-row bars of an FP8 output against the emulation and fp64.
+
+    Returns (GPU vs emulation, GPU vs fp64, emulation vs fp64), whole-sample relative RMS."""
     e_emu = rel_rms(got, emu)
     e_ref = rel_rms(got, ref)
     e_meth = rel_rms(emu, ref)
@@ -116,7 +227,34 @@ def check_fp8(got, emu, ref, label=""):
     assert np.all(np.isfinite(got)), label
     assert e_emu <= TOL_EMU, (label, e_emu)
     assert e_ref <= tol_fp64(e_meth), (label, e_ref, e_meth)
+    check_rows(got, emu, label, rows=rows, d=d, mode=mode, heads=heads, causal=causal)
     return e_emu, e_ref, e_meth
+
+
+LSE_BOUNDS = {"exact": (1 - 2.0 ** -4, 1 + 2.0 ** -4), "lean": (2.0 ** (-1 / 16), 1.0615 * 1.0625)}
+TOL_LSE_EMU_MAX = float(np.log(1.125))
+TOL_LSE_EMU_MEAN = 1e-3
+TOL_LSE_BF16 = 2e-4
+
+
+def lse_select(lse, heads=None, rows=None):
+    x = lse.cpu().numpy().astype(np.float64)        # (B, Hq, S)
+    if heads is not None:
+        x = x[:, list(heads)]
+    if rows is not None:
+        x = x[:, :, np.asarray(rows)]
+    return x
+
+
+def check_lse_fp8(got, emu, ref, mode, label):
+    assert np.all(np.isfinite(got)), label
+    d_emu = np.abs(got - emu)
+    d_ref = got - ref
+    lo, hi = LSE_BOUNDS[mode]
+    print(f"[parity] {label} lse: vs emulation max {d_emu.max():.2e} mean {d_emu.mean():.2e}; "
+          f"vs fp64 [{d_ref.min():+.4f}, {d_ref.max():+.4f}]")
+    assert d_emu.max() <= TOL_LSE_EMU_MAX and d_emu.mean() <= TOL_LSE_EMU_MEAN, label
+    assert d_ref.min() >= np.log(lo) - 2.0 ** -7 - 1e-3 and d_ref.max() <= np.log(hi) + 2.0 ** -7 + 1e-3, label
 
 
 __all__ = ["W", "rel_rms", "np", "torch", "binding"]

@@ -1,0 +1,113 @@
+"""GPU parity on inputs built to drive the paths that Gaussian inputs rarely reach:
+
+* the online rescale: key blocks whose scores jump by more than the reference slack
+  (16 log2 units on the FP8 path, 8 on the BF16 path) over the previous block, so that
+  the power-of-two reference of every row moves, and O and L are rescaled, at every block
+  ([MTP] "Per-block scaling and a rounded row sum": each 64-key block has its own power of
+  two; the running reference is this implementation's accumulator scale);
+* the E8M0 clamp: later blocks that sit more than 127 log2 units below the row's
+  reference, so that their scale exponent M - 8 - R falls below the E8M0 range;
+* the last, ragged query tile (S = 557: 45 rows past the last full 256-row tile, every
+  row's visible keys ending inside a block).
+
+Every output row is compared with the emulation (FP8, per-row bars of tests/parity.py) or
+with fp64 attention (BF16).  The premise of each case (the reference moves at every block,
+the exponent leaves the E8M0 range) is checked on the CPU first, with the oracle.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+from parity import (W, binding, check_fp8, gpu_select, oracle_bf16, oracle_fp8, rel_rms, row_rel_rms, run_bf16,
+                    run_fp8, TOL_BF16, TOL_BF16_ROW)
+from oracle.emulate import block_probabilities
+
+pytestmark = pytest.mark.gpu
+S = 557
+
+
+def _codes(x):
+    return x.clamp(-448.0, 448.0).to(torch.float8_e4m3fn).view(torch.uint8).contiguous()
+
+
+def _block_levels(dqk, kind, step):
+    """Per-block mean of every K channel, so that sum_c q_c k_c * sm * log2(e) (q ~ 1) moves by
+    `step` log2 units per block (ramp) or starts `step` units above the rest (drop)."""
+    unit = 1.0 / (math.log2(math.e) * math.sqrt(dqk))    # K level that adds one log2 unit
+    nb = (S + 63) // 64
+    if kind == "ramp":
+        return [b * step * unit for b in range(nb)]
+    return [step * unit] + [0.0] * (nb - 1)
+
+
+def _inputs(dqk, kind, step, Hq=4, Hkv=2, seed=31, bf16=False):
+    g = torch.Generator().manual_seed(seed)
+    q = 1.0 + 0.25 * torch.randn((1, S, Hq, dqk), generator=g)
+    lev = torch.tensor(_block_levels(dqk, kind, step)).repeat_interleave(64)[:S]
+    k = lev[None, :, None, None] + 0.5 * torch.randn((1, S, Hkv, dqk), generator=g)
+    v = torch.randn((1, S, Hkv, 128), generator=g)
+    if bf16:
+        return {"q": q.to(torch.bfloat16), "k": k.to(torch.bfloat16), "v": v.to(torch.bfloat16)}
+    return {"q8": _codes(q), "k8": _codes(k), "v8": _codes(v), "q_scale": 1.0, "k_scale": 1.0, "v_scale": 1.0}
+
+
+def _block_exponents(d, mode, i, h):
+    _, M = block_probabilities(d["q8"].numpy(), d["k8"].numpy(), 1.0, 1.0, p_mode=mode, i=i, h=h)
+    return M
+
+
+@pytest.mark.parametrize("mode", ["exact", "lean"])
+@pytest.mark.parametrize("dqk", [128, 192])
+def test_fp8_reference_moves_every_block(dqk, mode):
+    d = _inputs(dqk, "ramp", 20.0)
+    for h in range(4):
+        M = _block_exponents(d, mode, S - 1, h)
+        assert np.all(np.diff(M) > 16), M         # premise: every block moves the reference
+    got = gpu_select(run_fp8(d, mode))
+    emu, ref = oracle_fp8(d, mode)
+    check_fp8(got, emu, ref, f"ramp d{dqk} {mode}", d=d, mode=mode)
+
+
+@pytest.mark.parametrize("mode", ["exact", "lean"])
+@pytest.mark.parametrize("dqk", [128, 192])
+def test_fp8_e8m0_clamp(dqk, mode):
+    d = _inputs(dqk, "drop", 140.0)
+    for h in range(4):
+        M = _block_exponents(d, mode, S - 1, h)
+        assert np.all(M[1:] - 8 - M[0] < -127), M   # premise: later blocks leave the E8M0 range
+    out, lse = run_fp8(d, mode, return_lse=True)
+    got = gpu_select(out)
+    emu, ref = oracle_fp8(d, mode)
+    check_fp8(got, emu, ref, f"e8m0 clamp d{dqk} {mode}", d=d, mode=mode)
+    assert bool(torch.isfinite(lse).all())
+
+
+@pytest.mark.parametrize("kind,step", [("ramp", 12.0), ("drop", 140.0)])
+@pytest.mark.parametrize("dqk", [128, 192])
+def test_bf16_rescale_and_underflow(dqk, kind, step):
+    d = _inputs(dqk, kind, step, bf16=True)
+    q, k = d["q"].double().numpy(), d["k"].double().numpy()
+    t = (q[0, S - 1, 0] @ k[0, :, 0].T) * math.log2(math.e) / math.sqrt(dqk)
+    bmax = np.array([t[b:b + 64].max() for b in range(0, S, 64)])
+    if kind == "ramp":
+        assert np.all(np.diff(bmax) > 8), bmax     # premise: beyond the BF16 reference slack
+    else:
+        assert np.all(bmax[1:] - bmax[0] < -127), bmax
+    got = gpu_select(run_bf16(d))
+    ref = oracle_bf16(d)
+    e, er = rel_rms(got, ref), row_rel_rms(got, ref)
+    print(f"[parity] bf16 {kind} d{dqk}: vs fp64 {e:.2e}, per row max {er.max():.2e}")
+    assert np.all(np.isfinite(got)) and e <= TOL_BF16 and er.max() <= TOL_BF16_ROW
+
+
+@pytest.mark.parametrize("mode", ["exact", "lean"])
+@pytest.mark.parametrize("dqk", [128, 192])
+def test_fp8_last_ragged_tile_rows(dqk, mode):
+    d = W.make_fp8(W.Workload("ragged", 1, 4, 2, S, dqk, 128), seed=557)
+    got = gpu_select(run_fp8(d, mode))
+    emu, ref = oracle_fp8(d, mode)
+    tail = np.arange(512, S)
+    check_fp8(got[:, tail], emu[:, tail], ref[:, tail], f"last tile d{dqk} {mode}", rows=tail, d=d, mode=mode)
+    check_fp8(got, emu, ref, f"all rows d{dqk} {mode}", d=d, mode=mode)

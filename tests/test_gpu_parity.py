@@ -11,8 +11,8 @@ import numpy as np
 import pytest
 import torch
 
-from parity import (W, binding, check_fp8, gpu_select, oracle_bf16, oracle_fp8, rel_rms,
-                    row0_expected_fp8, run_bf16, run_fp8, TOL_BF16)
+from parity import (W, binding, check_fp8, gpu_select, oracle_bf16, oracle_fp8, rel_rms, row_rel_rms,
+                    row0_expected_fp8, run_bf16, run_fp8, NORTH_STAR_FP8, TOL_BF16, TOL_BF16_ROW)
 from oracle.e4m3 import bf16_rne, decode_e4m3
 
 pytestmark = pytest.mark.gpu
@@ -30,7 +30,7 @@ def test_tiny_full_tensor(mode):
     out = run_fp8(d, mode)
     got = gpu_select(out)
     emu, ref = oracle_fp8(d, mode)
-    check_fp8(got, emu, ref, f"tiny {mode}")
+    check_fp8(got, emu, ref, f"tiny {mode}", d=d, mode=mode)
     # row 0 has a single visible key: bit-exact
     exp0 = row0_expected_fp8(d)
     assert np.array_equal(got[:, 0].astype(np.float32), exp0), "row 0 not bit-exact"
@@ -49,7 +49,7 @@ def test_ragged_and_gqa_full_tensor(shape, mode):
     out = run_fp8(d, mode)
     got = gpu_select(out)
     emu, ref = oracle_fp8(d, mode)
-    check_fp8(got, emu, ref, f"{w.name} {mode}")
+    check_fp8(got, emu, ref, f"{w.name} {mode}", d=d, mode=mode)
     assert np.array_equal(got[:, 0].astype(np.float32), row0_expected_fp8(d)[:, np.arange(Hq) // (Hq // Hkv)])
 
 
@@ -92,24 +92,80 @@ def test_deterministic_over_repeated_launches(mode):
 
 
 def _sampled_heads(Hq):
-    return sorted({0, 1, Hq // 2, Hq - 1})
+    return sorted({0, Hq // 2, Hq - 1})
 
 
-@pytest.mark.parametrize("name,mode", [("gauss32k", "exact"), ("gauss32k", "lean"), ("mistral", "exact"),
-                                       ("mistral", "lean"), ("qwen", "lean"), ("mla", "exact"), ("mla", "lean")])
+# Full-size workloads in the launch configuration the benchmark times: 1024 query rows per
+# sampled head, 7/8 of them from the second half of the sequence (the long causal rows that
+# carry almost all of the work), checked row by row.
+FULL_ROWS = 1024
+_full_cache = {}
+
+
+def _full(name, mode):
+    key = (name, mode)
+    if key not in _full_cache:
+        _full_cache.clear()
+        w = W.WORKLOADS[name]
+        d = W.make_fp8(w)
+        out = run_fp8(d, mode)
+        rows = W.sample_rows_long(w.S, FULL_ROWS).numpy()
+        heads = _sampled_heads(w.Hq)
+        got = gpu_select(out, heads=heads, rows=rows)
+        finite = bool(torch.isfinite(out).all())
+        del out
+        emu, ref = oracle_fp8(d, mode, heads=heads, rows=rows)
+        _full_cache[key] = (w, d, rows, heads, got, emu, ref, finite)
+    return _full_cache[key]
+
+
+FULL_CASES = [("gauss32k", "exact"), ("gauss32k", "lean"), ("mistral", "exact"), ("mistral", "lean"),
+              ("qwen", "exact"), ("qwen", "lean"), ("mla", "exact"), ("mla", "lean")]
+
+
+@pytest.mark.parametrize("name,mode", FULL_CASES)
 def test_full_size_workloads_sampled(name, mode):
-    w = W.WORKLOADS[name]
-    d = W.make_fp8(w)
-    out = run_fp8(d, mode)
-    rows = W.sample_rows(w.S, 48).numpy()
-    heads = _sampled_heads(w.Hq)
-    got = gpu_select(out, heads=heads, rows=rows)
-    emu, ref = oracle_fp8(d, mode, heads=heads, rows=rows)
-    check_fp8(got, emu, ref, f"{name} {mode} (rows={len(rows)}, heads={heads})")
+    w, d, rows, heads, got, emu, ref, finite = _full(name, mode)
+    check_fp8(got, emu, ref, f"{name} {mode} (rows={len(rows)}, heads={heads})", rows=rows, d=d, mode=mode,
+              heads=heads)
     assert np.array_equal(got[:, 0].astype(np.float32),
                           row0_expected_fp8(d)[:, np.array(heads) // (w.Hq // w.Hkv)])
     # every output finite, not only the sampled ones
-    assert bool(torch.isfinite(out).all())
+    assert finite
+
+
+@pytest.mark.parametrize("name,mode", FULL_CASES)
+def test_north_star_fixed_fp64_bar(name, mode):
+    """The fixed 2e-2 relative-RMS bar against fp64 over the whole output tensor, reported on
+    its own.  The whole-tensor figure is estimated from every row below 256 plus a uniform
+    sample of 1024 later rows, each weighted by the number of rows it stands for (three heads).
+
+    Rounding every probability to e4m3 leaves a floor of ~2.65% (exact) and ~3.14% (Lean P)
+    on each long row of Gaussian-like inputs (closed form in tests/test_oracle_emulate.py), so
+    where the method itself - the emulation - is above the bar the GPU cannot meet it either:
+    that case is an expected failure, after checking that the GPU is at the method's error."""
+    w = W.WORKLOADS[name]
+    d = W.make_fp8(w)
+    out = run_fp8(d, mode)
+    rows, wts = W.sample_rows_strata(w.S)
+    rows, wts = rows.numpy(), wts.numpy()
+    heads = _sampled_heads(w.Hq)
+    got = gpu_select(out, heads=heads, rows=rows)
+    del out
+    emu, ref = oracle_fp8(d, mode, heads=heads, rows=rows)
+
+    def whole(x):
+        num = np.sum(wts[None, :, None] * np.sum((x - ref) ** 2, axis=-1))
+        return float(np.sqrt(num / np.sum(wts[None, :, None] * np.sum(ref ** 2, axis=-1))))
+    e_gpu, e_emu = whole(got), whole(emu)
+    late = rows >= w.S // 2
+    e_long = float(np.sqrt(np.mean(row_rel_rms(got[:, late], ref[:, late]) ** 2)))
+    print(f"[north-star] {name} {mode}: whole-tensor GPU vs fp64 {e_gpu:.4f} (emulation {e_emu:.4f}); "
+          f"rows in the second half, RMS of per-row errors {e_long:.4f}")
+    if e_gpu <= NORTH_STAR_FP8:
+        return
+    assert e_emu > NORTH_STAR_FP8 - 1e-3 and abs(e_gpu - e_emu) < 2e-3, (e_gpu, e_emu)
+    pytest.xfail(f"the method's own error against fp64 ({e_emu:.4f}) is above 2e-2; GPU {e_gpu:.4f}")
 
 
 # ----------------------------------------------------------------------------- BF16
@@ -122,8 +178,9 @@ def test_bf16_full_tensor(shape):
     got = gpu_select(run_bf16(d))
     ref = oracle_bf16(d)
     e = rel_rms(got, ref)
-    print(f"[parity] bf16 {shape}: vs fp64 {e:.2e}")
-    assert np.all(np.isfinite(got)) and e <= TOL_BF16
+    er = row_rel_rms(got, ref)
+    print(f"[parity] bf16 {shape}: vs fp64 {e:.2e}; per row max {er.max():.2e}")
+    assert np.all(np.isfinite(got)) and e <= TOL_BF16 and er.max() <= TOL_BF16_ROW
     # row 0: O_0 = v_0 * bf16(p)/p, within one bf16 ulp of v_0
     v0 = d["v"][:, 0].float().numpy()[:, np.arange(Hq) // (Hq // Hkv)]
     assert np.all(np.abs(got[:, 0] - v0) <= 2.0 ** -7 * np.abs(v0) + 1e-30)
@@ -151,10 +208,12 @@ def test_bf16_full_size_sampled(name):
     w = W.WORKLOADS[name]
     d = W.make_bf16(w)
     out = run_bf16(d)
-    rows = W.sample_rows(w.S, 48).numpy()
+    rows = W.sample_rows_long(w.S, FULL_ROWS).numpy()
     heads = _sampled_heads(w.Hq)
     got = gpu_select(out, heads=heads, rows=rows)
     ref = oracle_bf16(d, heads=heads, rows=rows)
     e = rel_rms(got, ref)
-    print(f"[parity] bf16 {name}: vs fp64 {e:.2e}")
+    er = row_rel_rms(got, ref)
+    print(f"[parity] bf16 {name}: vs fp64 {e:.2e}; per row median {np.median(er):.2e} max {er.max():.2e}")
     assert e <= TOL_BF16 and bool(torch.isfinite(out).all())
+    assert er.max() <= TOL_BF16_ROW

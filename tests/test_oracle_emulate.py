@@ -199,3 +199,43 @@ def test_unequal_causal_emulation_is_the_tail_of_the_full_problem(p_mode):
     tail, lt = emulate_fp8(q8[:, Sk - Sq:], k8, v8, qs, ks, vs, p_mode=p_mode, return_lse=True)
     assert np.max(np.abs(tail - full[:, Sk - Sq:])) <= 1e-13 * np.max(np.abs(full))
     assert np.max(np.abs(lt - lf[:, Sk - Sq:])) < 1e-12
+
+
+def _floor_closed_form(mode, n=200_000):
+    """Relative RMS error floor that rounding every probability to e4m3 leaves in a long row,
+    from the format definition alone.
+
+    With the log2 of a probability uniform modulo 1 (scores spread over many binades), its
+    rounded value is p (1 + delta(f)), f the fractional part.  Normalising by the sum of the
+    rounded values cancels the mean of delta, and for value rows independent of the scores the
+    output's relative RMS error is sd(delta) / (1 + mean(delta)).
+      exact: the 3-bit mantissa rounded to nearest, m = 2^f -> round(8 m) / 8;
+      Lean P: code = rint(8 f + 56) read back as 2^(code//8 - 7) (1 + (code % 8) / 8)."""
+    f = (np.arange(n) + 0.5) / n
+    m = 2.0 ** f
+    if mode == "exact":
+        val = np.round(8.0 * m) / 8.0
+    else:
+        code = np.rint(8.0 * f + 56.0)
+        val = 2.0 ** (np.floor(code / 8.0) - 7.0) * (1.0 + (code % 8.0) / 8.0)
+    delta = val / m - 1.0
+    return float(delta.std() / (1.0 + delta.mean()))
+
+
+@pytest.mark.parametrize("mode,expected", [("exact", 0.0265), ("lean", 0.0314)])
+def test_long_row_error_sits_at_e4m3_floor(mode, expected):
+    """The emulation's error against fp64, on long causal rows of a Gaussian workload, is the
+    closed-form e4m3 rounding floor (within 5%): the rounding, not anything else, sets it."""
+    from fp8_causal_prefill_tiled_amd import workloads as W
+    floor = _floor_closed_form(mode)
+    assert abs(floor - expected) < 2e-4
+    w = W.Workload("floor", 1, 1, 1, 8192, 128, 128)
+    d = W.make_fp8(w, seed=555)
+    rows = np.sort(np.random.default_rng(0).choice(np.arange(4096, 8192), 256, replace=False))
+    q8, k8, v8 = d["q8"].numpy(), d["k8"].numpy(), d["v8"].numpy()
+    ref = attention_fp64(dequantize(q8, d["q_scale"]), dequantize(k8, d["k_scale"]),
+                         dequantize(v8, d["v_scale"]), rows=rows)
+    emu = emulate_fp8(q8, k8, v8, d["q_scale"], d["k_scale"], d["v_scale"], p_mode=mode, rows=rows)
+    per_row = np.sqrt(np.sum((emu - ref) ** 2, axis=-1) / np.sum(ref ** 2, axis=-1))
+    measured = float(np.sqrt(np.mean(per_row ** 2)))
+    assert abs(measured / floor - 1.0) < 0.05, (mode, measured, floor)
