@@ -50,6 +50,12 @@ int check_common(const void* q, const void* k, const void* v, void* o, const flo
     // index and the head count must fit comfortably in 32-bit integers.
     const int64_t most = std::max<int64_t>(rows, rows_k);
     if (most > (int64_t)1 << 30) return fail(ATTN_E_UNSUPPORTED, "%s: %lld rows too many", who, (long long)most);
+    // The kernels address one 64-key block of K or V (64 rows of H*d elements) and the
+    // per-row strides inside it with 32-bit offsets and buffer ranges.
+    const int64_t block_bytes = (int64_t)64 * std::max(Hq, Hkv) * std::max(d_qk, d_v) * (int64_t)elem_qkv;
+    if (block_bytes >= ((int64_t)1 << 31))
+        return fail(ATTN_E_UNSUPPORTED, "%s: Hq=%d / Hkv=%d heads too many (a 64-row block exceeds 2 GiB)", who, Hq,
+                    Hkv);
     // one workgroup per (256-query tile, sequence, head)
     const int64_t grid = ((int64_t)S + 255) / 256 * B * Hq;
     if (grid > 0x7fffffffLL) return fail(ATTN_E_UNSUPPORTED, "%s: %lld workgroups too many", who, (long long)grid);

@@ -32,8 +32,10 @@
  *
  * Supported shapes: d_qk in {128, 192}, d_v == 128, Hq % Hkv == 0, S >= 1
  * (any S; the ragged last tile is masked), causal in {0, 1}, tensor pointers
- * 16-byte aligned.  B == 0 or S == 0 is an empty problem: ATTN_OK, nothing
- * launched.
+ * 16-byte aligned, and 64 * max(Hq, Hkv) * max(d_qk, d_v) * (bytes per Q/K/V
+ * element) below 2^31 (the kernels address a 64-key block with 32-bit
+ * offsets; larger head counts are ATTN_E_UNSUPPORTED).  B == 0 or S == 0 is an
+ * empty problem: ATTN_OK, nothing launched.
  *
  * Errors: every argument check happens on the host before any HIP call and
  * returns ATTN_E_INVALID_ARG (a malformed argument) or ATTN_E_UNSUPPORTED (a
@@ -124,7 +126,8 @@ int attn_fwd_fp8_lse(const void* q, const void* k, const void* v, void* o, float
  * q_scale, k_scale, v_scale: device pointers to one float each, 4-byte aligned,
  *      read by the kernel when it runs (values as for attn_fwd_fp8: finite and
  *      > 0; they cannot be checked on the host - other values give undefined
- *      outputs, never an out-of-bounds access).  The kernel forms
+ *      outputs, e.g. NaN from a zero scale times a masked score, never an
+ *      out-of-bounds access).  The kernel forms
  *      q_scale * k_scale * softmax_scale * log2(e) in double precision as the
  *      host does for attn_fwd_fp8, so both entry points give the same bits.
  * lse: NULL or as for attn_fwd_fp8_lse.  Other arguments, behaviour and errors

@@ -4,7 +4,7 @@ TEST INFRASTRUCTURE ONLY (see ``oracle/__init__.py``).
 
 The pages name the probability and input format "FP8 e4m3" ([KG-en] §"The Core
 Bottleneck"; [MTP] §TL;DR) and rely on one property of its bit pattern: read as
-an integer, the code grows by 8 each time the value doubles ([MTP] §"Lean P: one
+an unsigned integer, doubling a value adds 8 to its code ([MTP] §"Lean P: one
 multiply-add instead of an exponential").  The flavour is OCP e4m3fn: exponent
 bias 7, 3 mantissa bits, subnormals M*2^-9, no infinities, a single NaN pattern
 per sign (S.1111.111), largest finite 448 (a reading: the per-tensor scale

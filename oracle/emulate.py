@@ -11,9 +11,9 @@ in their order, in fp64 except where the method itself rounds:
    product has at most 8 significant bits and the sum spans < 53 bits).
    t_ij = s_ij * q_scale * k_scale * sm * log2(e) is the score in log2 units.
 2. Causal mask: keys j > i are excluded ([KG-en] §"Application Boundaries").
-3. Per-64-key-block power-of-2 scale.  Each 64-key block of probabilities is
-   scaled by a power of two before rounding, and the scaled matrix instruction
-   takes the factor back out ([MTP] §"Per-block scaling and a rounded row sum";
+3. Per-64-key-block power-of-2 scale.  Every block of 64 keys gets its own
+   power-of-two factor, applied to its probabilities ahead of the e4m3 rounding
+   and undone again by the block scale of the matrix instruction ([MTP] §"Per-block scaling and a rounded row sum";
    [KG-en] §"ZYFA's Technical Solutions").  Reading: the power is chosen per
    (query row, 64-key block) from M_ib = ceil(max_{j in block b, j<=i} t_ij),
    so that the block's largest probability lands in (128, 256] - the top binade
@@ -21,8 +21,8 @@ in their order, in fp64 except where the method itself rounds:
    the block's own integer maximum (independent of block order).
 4. Probabilities, one of two paths:
    * exact: p~_ij = e4m3_RNE(2^(t_ij - M_ib + 8)) - a true exponential, rounded;
-   * Lean P: the e4m3 code of 2^x is about 8x + const because the code grows
-     by 8 per doubling ([MTP] §"Lean P: one multiply-add instead of an
+   * Lean P: the e4m3 code of 2^x is about 8x + const because doubling a value
+     adds 8 to its code ([MTP] §"Lean P: one multiply-add instead of an
      exponential"; [KG-en] §"ZYFA's Technical Solutions").  With
      x = t_ij - M_ib + 8 and code(2^n) = 8n + 56 the code is the single
      multiply-add A*s_ij + B_ib, A = 8*q_scale*k_scale*sm*log2(e),

@@ -232,8 +232,7 @@ def check_fp8(got, emu, ref, label="", rows=None, d=None, mode=None, heads=None,
 
 
 LSE_BOUNDS = {"exact": (1 - 2.0 ** -4, 1 + 2.0 ** -4), "lean": (2.0 ** (-1 / 16), 1.0615 * 1.0625)}
-TOL_LSE_EMU_MAX = float(np.log(1.125))
-TOL_LSE_EMU_MEAN = 1e-3
+TOL_LSE_ROW = 2e-4
 TOL_LSE_BF16 = 2e-4
 
 
@@ -246,14 +245,40 @@ def lse_select(lse, heads=None, rows=None):
     return x
 
 
-def check_lse_fp8(got, emu, ref, mode, label):
+def check_lse_fp8(got, emu, ref, mode, label, d=None, rows=None, heads=None, causal=True):
+    """FP8 log-sum-exp (B, heads, rows) against the emulation's log of the same denominator and
+    against fp64.
+
+    Per row: within TOL_LSE_ROW of the emulation (fp32 scores and sums), unless rounding
+    decisions that are ambiguous at the dot product's precision explain the difference: a
+    flipped probability changes the denominator L by |W_alt - W|, so the row passes if
+    |lse - lse_emu| <= TOL_LSE_ROW - ln(1 - sum_alt |W_alt - W| / L) over every alternative of
+    the row (oracle.emulate.rounding_alternatives; needs ``d`` and the row and head indices).
+    Median over the rows <= TOL_LSE_ROW."""
     assert np.all(np.isfinite(got)), label
     d_emu = np.abs(got - emu)
     d_ref = got - ref
     lo, hi = LSE_BOUNDS[mode]
-    print(f"[parity] {label} lse: vs emulation max {d_emu.max():.2e} mean {d_emu.mean():.2e}; "
+    rows_idx = np.arange(got.shape[2]) if rows is None else np.asarray(rows)
+    heads_idx = np.arange(got.shape[1]) if heads is None else np.asarray(heads)
+    n_expl = 0
+    for b, hi_, ri in np.argwhere(d_emu > TOL_LSE_ROW):
+        where = (label, "lse row", int(b), int(rows_idx[ri]), int(heads_idx[hi_]), float(d_emu[b, hi_, ri]))
+        assert d is not None, where
+        info = rounding_alternatives(d["q8"].numpy(), d["k8"].numpy(), d["v8"].numpy(), d["q_scale"],
+                                     d["k_scale"], d["v_scale"], p_mode=mode, b=int(b), i=int(rows_idx[ri]),
+                                     h=int(heads_idx[hi_]), causal=causal, kappa=KAPPA)
+        per_key = {}
+        for j, wa in info["alt"]:
+            per_key[j] = max(per_key.get(j, 0.0), abs(wa - info["weight"][j]))
+        x = sum(per_key.values()) / info["weight"].sum()
+        bound = TOL_LSE_ROW + (-np.log1p(-x) if x < 1 else np.inf)
+        assert d_emu[b, hi_, ri] <= bound, where + (bound,)
+        n_expl += 1
+    print(f"[parity] {label} lse: vs emulation median {np.median(d_emu):.2e} max {d_emu.max():.2e} "
+          f"({n_expl} rows above {TOL_LSE_ROW:.0e} within their alternative-rounding bound); "
           f"vs fp64 [{d_ref.min():+.4f}, {d_ref.max():+.4f}]")
-    assert d_emu.max() <= TOL_LSE_EMU_MAX and d_emu.mean() <= TOL_LSE_EMU_MEAN, label
+    assert np.median(d_emu) <= TOL_LSE_ROW, label
     assert d_ref.min() >= np.log(lo) - 2.0 ** -7 - 1e-3 and d_ref.max() <= np.log(hi) + 2.0 ** -7 + 1e-3, label
 
 

@@ -68,6 +68,8 @@ def bf16(**kw):
     (dict(q_scale=1e-30, k_scale=1e-30), INVALID),
     (dict(q=Q + 8), INVALID), (dict(o=O + 2), INVALID),
     (dict(o=Q + 4096), INVALID),                      # output overlaps Q
+    (dict(Hq=262144, Hkv=262144), UNSUPPORTED),       # a 64-key block of K past 2 GiB (32-bit offsets)
+    (dict(Hq=174763, Hkv=174763, d_qk=192), UNSUPPORTED),
     (dict(S=0, q=0, k=0, v=0, o=0), OK), (dict(B=0, q=0, k=0, v=0, o=0), OK),  # empty: nothing launched
 ])
 def test_fp8_host_validation(lib, kw, status):
@@ -82,6 +84,7 @@ def test_fp8_host_validation(lib, kw, status):
     (dict(k=0), INVALID), (dict(Hq=5, Hkv=2), INVALID), (dict(d_qk=256), UNSUPPORTED),
     (dict(causal=3), INVALID), (dict(softmax_scale=math.inf), INVALID), (dict(k=K + 1), INVALID),
     (dict(o=V + 64), INVALID), (dict(S=0, q=0, k=0, v=0, o=0), OK),
+    (dict(Hq=131072, Hkv=131072), UNSUPPORTED),       # bf16: a 64-key block of K past 2 GiB
 ])
 def test_bf16_host_validation(lib, kw, status):
     assert bf16(**kw) == status

@@ -171,7 +171,7 @@ def test_flash_attn_func_fp8_against_oracle(dqk, mode, scales, compiled):
     emu, ref, lemu, lref = oracle_fp8(d, mode, with_lse=True)
     label = f"flash_attn_func fp8 d{dqk} {mode} {scales} scales{' compiled' if compiled else ''}"
     check_fp8(gpu_select(out), emu, ref, label, d=d, mode=mode)
-    check_lse_fp8(lse_select(lse), lemu, lref, mode, label)
+    check_lse_fp8(lse_select(lse), lemu, lref, mode, label, d=d)
 
 
 @pytest.mark.parametrize("compiled", [False, True])

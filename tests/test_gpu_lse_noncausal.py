@@ -7,12 +7,13 @@ Bars (derived from the arithmetic):
 * O: the same as for the causal path (GPU vs emulation <= 5e-3 relative RMS, vs
   fp64 the method's own error plus output rounding; BF16 <= 4e-3 vs fp64).
 * FP8 lse vs the emulation's log of the same rounded-probability denominator:
-  fp32 scores and sums leave ~1e-6; a probability whose e4m3 rounding flips
-  between fp32 and fp64 moves by one e4m3 step, at most 1/8 of itself, so no
-  row can be off by more than ln(1 + 1/8), and the mean stays below 1e-3.
+  fp32 scores and sums leave ~1e-6, so every row is within 2e-4 unless a
+  probability whose rounding is ambiguous at the FP8 dot product's precision
+  took its other code; such a row must stay within the bound that all of its
+  ambiguous probabilities together allow (tests/parity.py, check_lse_fp8).
 * FP8 lse vs the fp64 log-sum-exp: the emulation's own bounds (each rounded
   probability within [lo, hi] of its true value when normal, 2^-7 for the
-  subnormal rest), plus the 1e-3 above.
+  subnormal rest), plus 1e-3.
 * BF16 lse vs fp64 on the bf16 inputs: fp32 scores, exponentials and sums only,
   <= 2e-4 absolute.
 """
@@ -47,7 +48,7 @@ def test_fp8_output_and_lse_full_tensor(shape, mode, causal):
     emu, ref, lemu, lref = oracle_fp8(d, mode, causal=causal, with_lse=True)
     label = f"{w.name} {mode} causal={causal}"
     check_fp8(gpu_select(out), emu, ref, label, d=d, mode=mode, causal=causal)
-    check_lse_fp8(lse_select(lse), lemu, lref, mode, label)
+    check_lse_fp8(lse_select(lse), lemu, lref, mode, label, d=d, causal=causal)
 
 
 @pytest.mark.parametrize("mode", MODES)
@@ -103,7 +104,8 @@ def test_fp8_noncausal_full_size_sampled(name, mode):
     label = f"{name} {mode} non-causal (rows={len(rows)}, heads={heads})"
     check_fp8(gpu_select(out, heads=heads, rows=rows), emu, ref, label, rows=rows, d=d, mode=mode, heads=heads,
               causal=False)
-    check_lse_fp8(lse_select(lse, heads=heads, rows=rows), lemu, lref, mode, label)
+    check_lse_fp8(lse_select(lse, heads=heads, rows=rows), lemu, lref, mode, label, d=d, rows=rows, heads=heads,
+                  causal=False)
     assert bool(torch.isfinite(out).all()) and bool(torch.isfinite(lse).all())
 
 
@@ -117,7 +119,8 @@ def test_fp8_causal_lse_full_size_sampled(name, mode):
     emu, ref, lemu, lref = oracle_fp8(d, mode, heads=heads, rows=rows, with_lse=True)
     check_fp8(gpu_select(out, heads=heads, rows=rows), emu, ref, f"{name} {mode} causal lse call", rows=rows, d=d,
               mode=mode, heads=heads)
-    check_lse_fp8(lse_select(lse, heads=heads, rows=rows), lemu, lref, mode, f"{name} {mode} causal")
+    check_lse_fp8(lse_select(lse, heads=heads, rows=rows), lemu, lref, mode, f"{name} {mode} causal", d=d, rows=rows,
+                  heads=heads)
     assert bool(torch.isfinite(lse).all())
 
 

@@ -1,7 +1,7 @@
 """GPU parity of the Hadamard rotation + per-tensor FP8 quantisation of Q and K
 (attn_rotate_quant_bf16, through the C ABI) against oracle/rotate.py, and its
 end-to-end effect on the FP8 attention ([MTP] section "How accurate is ZYFA's FP8
-attention?": the rotation roughly halves the input error)."""
+attention?": the rotation cuts the input error to about half)."""
 import numpy as np
 import pytest
 import torch

@@ -26,7 +26,7 @@ def test_decode_exhaustive_matches_torch():
 
 
 def test_closed_forms():
-    # code(2^n) = 8n + 56 for every normal power of two: the "grows by 8 per doubling" law.
+    # code(2^n) = 8n + 56 for every normal power of two: doubling adds 8 to the code.
     for n in range(-6, 9):
         assert encode_e4m3_rne(2.0 ** n) == 8 * n + 56
         assert decode_e4m3(np.uint8(8 * n + 56)) == 2.0 ** n

@@ -65,7 +65,7 @@ def test_row0_is_v0_and_constant_v_is_exact(p_mode):
 
 
 def test_lean_code_law_is_8x_plus_constant():
-    # The e4m3 code grows by 8 per doubling: at integer exponents Lean P is exact.
+    # Doubling a value adds 8 to its e4m3 code: at integer exponents Lean P is exact.
     for n in range(-6, 9):
         assert encode_probability_lean(float(n)) == 8 * n + 56 == encode_probability_exact(float(n))
     # between integers it is the chord of 2^x (never below, at most 6.15% above, before rounding)

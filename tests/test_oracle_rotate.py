@@ -82,8 +82,8 @@ def _attention_error(w, rotate_first):
 
 
 def test_rotation_cuts_the_input_error_with_outlier_channels():
-    # The pages: a Hadamard rotation of Q and K roughly halves the input error on a real
-    # model; on Mistral-shaped inputs (4 outlier channels x8) it must at least do that.
+    # The pages report the rotation cutting the input-quantisation error to about a half on a
+    # real model; on Mistral-shaped inputs (4 outlier channels x8) it must do at least that.
     w = W.WORKLOADS["mistral"].with_(S=384, Hq=4, Hkv=2)
     assert _attention_error(w, True) < 0.5 * _attention_error(w, False)
 
