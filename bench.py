@@ -40,9 +40,16 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-rotate", action="store_true",
                     help="skip timing the Hadamard rotation + quantisation of Q and K")
-    ap.add_argument("--input-study", action="store_true",
+    ap.add_argument("--input-study", action="store_true", default=True,
                     help="also time the FP8 kernel on low-bit-activity inputs (sparse, zero Q) with power "
-                         "and clock samples (reported under 'input_study')")
+                         "and clock samples (reported under 'input_study'; on by default)")
+    ap.add_argument("--no-input-study", dest="input_study", action="store_false")
+    ap.add_argument("--extra-workloads", default="mla:fp8,qwen:bf16",
+                    help="comma-separated workload:dtype pairs timed after the headline and reported under "
+                         "'other_workloads' (empty to skip); FP8 ones run both probability paths")
+    ap.add_argument("--emu-rows", type=int, default=256,
+                    help="long query rows per head on which the CPU leg also runs the step-by-step emulation "
+                         "of the FP8 method (0 to skip)")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
                     help="after timing, run one device-to-device copy of this many MiB "
                          "(a known-size kernel for scaling HBM byte counters)")
@@ -264,6 +271,7 @@ def input_study(w, d, q, k, v, out, stream, flops, steps, warmup, modes, paths):
 
     variants = {"sparse90": (sparse_codes(q), sparse_codes(k), sparse_codes(v)),
                 "zero_q": (torch.zeros_like(q), k, v)}
+    out = torch.empty_like(out)       # the headline output stays as it is
     res = {"gaussian": {m: {"tflops": paths[m]["tflops"], **paths[m]["energy"]} for m in modes}}
     sampler = PowerClockSampler()
     for name, (qq, kk, vv) in variants.items():
@@ -279,7 +287,104 @@ def input_study(w, d, q, k, v, out, stream, flops, steps, warmup, modes, paths):
     return res
 
 
-def cpu_baseline(w, d, outs, seconds, dtype):
+def other_workloads(spec, steps, warmup, stream):
+    """Throughput, power and clock of the kernels on further workloads (BASELINE configs other than
+    the headline): each runs alone on freshly drawn inputs, FP8 ones on both probability paths."""
+    import torch
+    from fp8_causal_prefill_tiled_amd import binding
+    from fp8_causal_prefill_tiled_amd import workloads as W
+    res = {}
+    dev = torch.device("cuda:0")
+    sampler = PowerClockSampler()
+    for item in [x for x in spec.split(",") if x]:
+        name, dtype = item.split(":")
+        w = W.WORKLOADS[name]
+        flops, peak = w.causal_flops, PEAK_TFLOPS[dtype]
+        out = torch.empty((w.B, w.S, w.Hq, w.d_v), dtype=torch.bfloat16, device=dev)
+        if dtype == "fp8":
+            d = W.make_fp8(w)
+            q, k, v = (d[n].to(dev) for n in ("q8", "k8", "v8"))
+            fns = {m: (lambda m=m: binding.attn_fwd_fp8(q, k, v, d["q_scale"], d["k_scale"], d["v_scale"],
+                                                        p_mode=m, out=out, stream=stream)) for m in ("lean", "exact")}
+        else:
+            d = W.make_bf16(w)
+            q, k, v = (d[n].to(dev) for n in ("q", "k", "v"))
+            fns = {"bf16": lambda: binding.attn_fwd_bf16(q, k, v, out=out, stream=stream)}
+        torch.cuda.synchronize()
+        entry = {"workload": name, "dtype": dtype, "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv, "S": w.S, "d_qk": w.d_qk,
+                 "d_v": w.d_v, "causal_tflop_per_step": flops / 1e12, "paths": {}}
+        for m, fn in fns.items():
+            for _ in range(3 * warmup):           # settle the power and clock readings first
+                fn()
+            wall, per = time_launches(fn, steps, warmup, stream, sampler)
+            avg_ms = sum(per) / len(per)
+            entry["paths"][m] = {"tflops": flops * steps / wall / 1e12, "kernel_ms_avg": avg_ms,
+                                 "frac_of_peak": flops / (avg_ms * 1e-3) / 1e12 / peak,
+                                 "energy": sampler.summary(flops * steps, wall)}
+        res[f"{name}_{dtype}"] = entry
+        del q, k, v, out, d
+        torch.cuda.synchronize()
+    return res
+
+
+def _e4m3_floor(mode, n=200_000):
+    """Closed-form relative RMS error floor of rounding every probability of a long row to e4m3
+    (log2 of the probability uniform modulo 1; the rounded-sum normalisation cancels the mean):
+    sd(delta) / (1 + mean(delta)), delta the relative rounding error of one probability."""
+    import numpy as np
+    f = (np.arange(n) + 0.5) / n
+    m = 2.0 ** f
+    if mode == "exact":
+        val = np.round(8.0 * m) / 8.0
+    else:
+        code = np.rint(8.0 * f + 56.0)
+        val = 2.0 ** (np.floor(code / 8.0) - 7.0) * (1.0 + (code % 8.0) / 8.0)
+    delta = val / m - 1.0
+    return float(delta.std() / (1.0 + delta.mean()))
+
+
+def emulation_leg(w, d, outs, n_rows):
+    """The step-by-step emulation of the FP8 method (oracle/emulate.py) and fp64 attention on n_rows
+    query rows drawn from the second half of the sequence (long causal rows) for three heads: the
+    method's own error against fp64 there, the GPU's distance to the emulation, and the closed-form
+    e4m3 floor the method's error should sit at."""
+    import numpy as np
+    from oracle.attention64 import attention_fp64, dequantize
+    from oracle.emulate import emulate_fp8
+    g = np.random.default_rng(20261202)
+    rows = np.sort(g.choice(np.arange(w.S // 2, w.S), size=min(n_rows, w.S // 2), replace=False))
+    heads = [0, w.Hq // 2, w.Hq - 1]
+    t0 = time.perf_counter()
+    res = {m: {"emu": [], "gpu": [], "gpu_emu": []} for m in outs}
+    for h in heads:
+        gk = h // (w.Hq // w.Hkv)
+        q8, k8, v8 = d["q8"][:, :, h:h + 1].numpy(), d["k8"][:, :, gk:gk + 1].numpy(), d["v8"][:, :, gk:gk + 1].numpy()
+        ref = attention_fp64(dequantize(q8, d["q_scale"]), dequantize(k8, d["k_scale"]), dequantize(v8, d["v_scale"]),
+                             rows=rows)
+        for m, o in outs.items():
+            emu = emulate_fp8(q8, k8, v8, d["q_scale"], d["k_scale"], d["v_scale"], p_mode=m, rows=rows)
+            got = o[:, rows, h:h + 1].astype(np.float64)
+
+            def per_row(x, y):
+                return np.sqrt(np.sum((x - y) ** 2, axis=-1) / np.sum(y ** 2, axis=-1)).reshape(-1)
+            res[m]["emu"].append(per_row(emu, ref))
+            res[m]["gpu"].append(per_row(got, ref))
+            res[m]["gpu_emu"].append(per_row(got, emu))
+    out = {"rows": f"{len(rows)} rows drawn uniformly from {w.S // 2}..{w.S - 1} x heads {heads}",
+           "seconds": time.perf_counter() - t0}
+    for m, r in res.items():
+        e, gg, ge = (np.concatenate(r[k]) for k in ("emu", "gpu", "gpu_emu"))
+        out[m] = {"emulation_rel_rms_vs_fp64": float(np.sqrt(np.mean(e ** 2))),
+                  "gpu_rel_rms_vs_fp64": float(np.sqrt(np.mean(gg ** 2))),
+                  "gpu_rel_rms_vs_emulation": float(np.sqrt(np.mean(ge ** 2))),
+                  "gpu_vs_emulation_per_row_median": float(np.median(ge)),
+                  "gpu_vs_emulation_per_row_max": float(np.max(ge)),
+                  "e4m3_floor_closed_form": _e4m3_floor(m),
+                  "note": "RMS over rows of each row's relative RMS error (rows weighted equally)"}
+    return out
+
+
+def cpu_baseline(w, d, outs, seconds, dtype, emu_rows=0):
     """Time the CPU oracle (fp64 attention) on a bounded sample of the same workload and
     compare the GPU outputs on those rows.  Returns the cpu_baseline object.
 
@@ -344,6 +449,7 @@ def cpu_baseline(w, d, outs, seconds, dtype):
                   "per_head_max_rel_rms_dequantised": max(rel(v) for v in e["head"].values())}
               for m, e in err.items()}
     tiny = _cpu_tiny_full()
+    emu = emulation_leg(w, d, outs, emu_rows) if dtype == "fp8" and emu_rows > 0 else None
     return {
         "value": flops / el / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
         "tiny_full": tiny,
@@ -352,6 +458,7 @@ def cpu_baseline(w, d, outs, seconds, dtype):
                   f"{el:.1f} s of oracle time; FLOPs counted 2*(i+1)*(d_qk+d_v) per row i",
         "gpu_rel_rms_vs_oracle_on_sample": errors[next(iter(outs))]["rel_rms_vs_fp64_dequantised_inputs"],
         "gpu_error_on_sample": errors,
+        "method_error_on_long_rows": emu,
         "cpu_model": _cpu_model(),
         "os_cpu_count": os.cpu_count(),
     }
@@ -479,11 +586,17 @@ def main():
             torch.cuda.synchronize()
             outs[m] = o2.float().cpu().numpy()
             del o2
-        cpu = cpu_baseline(w, d, outs, args.cpu_seconds, args.dtype)
+        cpu = cpu_baseline(w, d, outs, args.cpu_seconds, args.dtype, args.emu_rows)
 
     rot = None
     if args.dtype == "fp8" and not args.no_rotate:
         rot = rotate_quant_timing(w, args.steps, args.warmup, stream, head["kernel_ms_avg"])
+
+    others = None
+    if args.extra_workloads:
+        del q, k, v
+        torch.cuda.synchronize()
+        others = other_workloads(args.extra_workloads, args.steps, args.warmup, stream)
 
     pages = PAGES_TFLOPS.get((w.name, args.dtype))
     res = {
@@ -511,6 +624,7 @@ def main():
         "paths": paths,
         "rotate_quant": rot,
         "input_study": study,
+        "other_workloads": others,
         "sclk_mhz": {"before": clk_before, "after": clk_after},
         "cpu_baseline": cpu,
     }

@@ -45,3 +45,10 @@ def test_cpu_baseline_reports_both_paths_errors_on_a_small_workload():
     # against the unquantised draws the error includes the e4m3 input rounding
     assert e["exact"]["rel_rms_vs_fp64_unquantised_inputs"] > 0.005
     assert r["gpu_rel_rms_vs_oracle_on_sample"] == e["lean"]["rel_rms_vs_fp64_dequantised_inputs"]
+
+
+def test_e4m3_floor_values():
+    # the benchmark's closed-form floor equals the one the oracle's emulation is pinned to
+    import bench
+    assert abs(bench._e4m3_floor("exact") - 0.0265) < 2e-4
+    assert abs(bench._e4m3_floor("lean") - 0.0314) < 2e-4
