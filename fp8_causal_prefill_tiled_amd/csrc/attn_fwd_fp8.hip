@@ -777,74 +777,90 @@ __global__ void __launch_bounds__(512) fp8_causal_fwd_pair(Fp8Params a) {
 #pragma unroll
     for (int bl = 0; bl < NB; ++bl) sb[bl] = 127;
 
-    // ---- the vector phase of block pair p: mask (blocks from the diagonal one on),
-    // block exponents M (row max over each block), the reference decision for the
-    // pair, probability bytes, the rare exact rescale of O and L when the
-    // power-of-two reference moves (by more than kRefSlack), E8M0 scale bytes.
+    // ---- the vector phase of block pair p: masks (pairs from the diagonal one on), block
+    // exponents M (row max over each block), the reference decision for the pair,
+    // probability bytes, the rare exact rescale of O and L when the power-of-two
+    // reference moves (by more than kRefSlack), E8M0 scale bytes.  The two blocks'
+    // dependency chains (the row maxima, the byte packing of each word) are interleaved:
+    // a wave issues a dependent vector instruction more slowly than an independent one.
     auto valu_phase = [&](int p) {
-        float M[NB];
+        // masks: only pairs that reach the diagonal (or the ragged last block); the
+        // formula leaves a block that lies wholly inside the visible range unchanged
+        if (NB * p + NB - 1 >= jdiag) {
+            const int qlim = CAUSAL ? min(qabs + qoff, Sk - 1) : Sk - 1;
 #pragma unroll
-        for (int bl = 0; bl < NB; ++bl) {
-            const int jb = NB * p + bl;
-            f32x16& s0 = sc[bl][0];
-            f32x16& s1 = sc[bl][1];
-            if (jb >= jdiag) {
-                // key kb0 + off(r) + 4hh is visible iff off(r) <= qlim - kb0 - 4hh, qlim the
-                // last key the query sees
-                const int qlim = CAUSAL ? min(qabs + qoff, Sk - 1) : Sk - 1;
-                const int lim = qlim - jb * KB - 4 * hh;
+            for (int bl = 0; bl < NB; ++bl) {
+                const int lim = qlim - (NB * p + bl) * KB - 4 * hh;
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
                     const int off = 8 * (r >> 2) + (r & 3);
-                    s0[r] = off <= lim ? s0[r] : -INFINITY;
-                    s1[r] = off + 32 <= lim ? s1[r] : -INFINITY;
+                    sc[bl][0][r] = off <= lim ? sc[bl][0][r] : -INFINITY;
+                    sc[bl][1][r] = off + 32 <= lim ? sc[bl][1][r] : -INFINITY;
                 }
             }
-            float mx = -INFINITY;
+        }
+        // row maxima of the blocks: independent chains, interleaved
+        float mx[NB], M[NB];
 #pragma unroll
-            for (int r = 0; r < 16; ++r) mx = fmaxf(fmaxf(mx, s0[r]), s1[r]);
-            mx = pair_max(mx);
-            M[bl] = fmaxf(ceilf(mx * sc_c), -1.0e30f);  // floor: rows with no visible key here
+        for (int bl = 0; bl < NB; ++bl) mx[bl] = fmaxf(sc[bl][0][0], sc[bl][1][0]);
+#pragma unroll
+        for (int r = 1; r < 16; ++r)
+#pragma unroll
+            for (int bl = 0; bl < NB; ++bl) mx[bl] = fmaxf(fmaxf(mx[bl], sc[bl][0][r]), sc[bl][1][r]);
+#pragma unroll
+        for (int bl = 0; bl < NB; ++bl) {
+            mx[bl] = pair_max(mx[bl]);
+            M[bl] = fmaxf(ceilf(mx[bl] * sc_c), -1.0e30f);  // floor: rows with no visible key here
         }
         float Mmax = M[0];
 #pragma unroll
         for (int bl = 1; bl < NB; ++bl) Mmax = fmaxf(Mmax, M[bl]);
         const bool need = Mmax > ref + kRefSlack;
         const float nref = need ? Mmax : ref;
+        float bias[NB];
 #pragma unroll
         for (int bl = 0; bl < NB; ++bl) {
-            const float bias = PMODE == 0 ? 8.0f - M[bl] : 120.0f - 8.0f * M[bl];
+            bias[bl] = PMODE == 0 ? 8.0f - M[bl] : 120.0f - 8.0f * M[bl];
             // E8M0 byte of 2^(M-8-nref), exponent clamped to [-127, 127]: all terms are
             // integers in float, so one median and one conversion give it exactly
             sb[bl] = (int)__builtin_amdgcn_fmed3f(M[bl] - nref + 119.0f, 0.0f, 254.0f);
-            int pw[8];
-            if (PMODE == 0) {
-#pragma unroll
-                for (int q4 = 0; q4 < 8; ++q4) {
-                    const f32x16& x = q4 < 4 ? sc[bl][0] : sc[bl][1];
-                    const int e = 4 * (q4 & 3);
-                    const float p0 = __builtin_amdgcn_exp2f(fmaf(x[e + 0], sc_c, bias));
-                    const float p1 = __builtin_amdgcn_exp2f(fmaf(x[e + 1], sc_c, bias));
-                    const float p2 = __builtin_amdgcn_exp2f(fmaf(x[e + 2], sc_c, bias));
-                    const float p3 = __builtin_amdgcn_exp2f(fmaf(x[e + 3], sc_c, bias));
-                    const int wd = __builtin_amdgcn_cvt_pk_fp8_f32(p0, p1, 0, false);
-                    pw[q4] = __builtin_amdgcn_cvt_pk_fp8_f32(p2, p3, wd, true);
-                }
-            } else {
-#pragma unroll
-                for (int q4 = 0; q4 < 8; ++q4) {
-                    const f32x16& x = q4 < 4 ? sc[bl][0] : sc[bl][1];
-                    const int e = 4 * (q4 & 3);
-                    unsigned wd = 0;
-                    wd = __builtin_amdgcn_cvt_pk_u8_f32(fmaf(x[e + 0], sc_a8, bias), 0, wd);
-                    wd = __builtin_amdgcn_cvt_pk_u8_f32(fmaf(x[e + 1], sc_a8, bias), 1, wd);
-                    wd = __builtin_amdgcn_cvt_pk_u8_f32(fmaf(x[e + 2], sc_a8, bias), 2, wd);
-                    wd = __builtin_amdgcn_cvt_pk_u8_f32(fmaf(x[e + 3], sc_a8, bias), 3, wd);
-                    pw[q4] = (int)wd;
-                }
-            }
-            pv[bl] = i32x8{pw[0], pw[1], pw[2], pw[3], pw[4], pw[5], pw[6], pw[7]};
         }
+        // probability bytes: byte e of all 16 words, then byte e + 1, ... (each word packs its
+        // four bytes in sequence; stepping through the words keeps those chains apart)
+        int pw[NB][8];
+        if (PMODE == 0) {
+#pragma unroll
+            for (int q4 = 0; q4 < 8; ++q4)
+#pragma unroll
+                for (int bl = 0; bl < NB; ++bl) {
+                    const f32x16& x = q4 < 4 ? sc[bl][0] : sc[bl][1];
+                    const int e = 4 * (q4 & 3);
+                    const float p0 = __builtin_amdgcn_exp2f(fmaf(x[e + 0], sc_c, bias[bl]));
+                    const float p1 = __builtin_amdgcn_exp2f(fmaf(x[e + 1], sc_c, bias[bl]));
+                    const float p2 = __builtin_amdgcn_exp2f(fmaf(x[e + 2], sc_c, bias[bl]));
+                    const float p3 = __builtin_amdgcn_exp2f(fmaf(x[e + 3], sc_c, bias[bl]));
+                    const int wd = __builtin_amdgcn_cvt_pk_fp8_f32(p0, p1, 0, false);
+                    pw[bl][q4] = __builtin_amdgcn_cvt_pk_fp8_f32(p2, p3, wd, true);
+                }
+        } else {
+#pragma unroll
+            for (int g = 0; g < 8; g += 2) {   // two words of each block at a time
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+#pragma unroll
+                    for (int q4 = g; q4 < g + 2; ++q4)
+#pragma unroll
+                        for (int bl = 0; bl < NB; ++bl) {
+                            const f32x16& x = q4 < 4 ? sc[bl][0] : sc[bl][1];
+                            const float y = fmaf(x[4 * (q4 & 3) + e], sc_a8, bias[bl]);
+                            pw[bl][q4] = (int)__builtin_amdgcn_cvt_pk_u8_f32(y, e, e == 0 ? 0u : (unsigned)pw[bl][q4]);
+                        }
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        }
+#pragma unroll
+        for (int bl = 0; bl < NB; ++bl)
+            pv[bl] = i32x8{pw[bl][0], pw[bl][1], pw[bl][2], pw[bl][3], pw[bl][4], pw[bl][5], pw[bl][6], pw[bl][7]};
         if (__ballot(need)) {
             vacc_settle(o, lsum);
             const float f = __builtin_amdgcn_exp2f(ref - nref);   // exactly 1 for rows that do not move
