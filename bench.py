@@ -206,6 +206,23 @@ def time_launches(fn, steps, warmup, stream, sampler=None):
 HBM_PEAK_GBPS = 8000.0
 
 
+def time_batched(fn, steps, warmup, stream):
+    """Average ms per call of `steps` back-to-back calls between one pair of HIP events on the
+    launch stream (for kernels of tens of microseconds, where an event pair around every
+    call would add its own overhead to each)."""
+    import torch
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(steps):
+        fn()
+    e1.record(stream)
+    e1.synchronize()
+    return e0.elapsed_time(e1) / steps
+
+
 def rotate_quant_timing(w, steps, warmup, stream, attn_ms):
     """Time attn_rotate_quant_bf16 on bf16 tensors of the workload's Q and K shapes
     (seeded N(0,1), resident in HBM).  HBM roofline of the pass: algorithmic bytes =
@@ -220,24 +237,21 @@ def rotate_quant_timing(w, steps, warmup, stream, attn_ms):
         x = torch.randn((w.B, w.S, h, w.d_qk), generator=g, device=dev, dtype=torch.float32).to(torch.bfloat16)
         out = torch.empty(x.shape, dtype=torch.uint8, device=dev)
         sc = torch.empty(1, dtype=torch.float32, device=dev)
-        _, per = time_launches(lambda: binding.rotate_quant_bf16(x, out=out, scale=sc, stream=stream),
-                               steps, warmup, stream)
-        ms = sum(per) / len(per)
+        ms = time_batched(lambda: binding.rotate_quant_bf16(x, out=out, scale=sc, stream=stream), steps, warmup,
+                          stream)
         nbytes = x.numel() * 3
         res[name] = {"shape": list(x.shape), "kernel_ms_avg": ms, "algorithmic_bytes": nbytes,
                      "achieved_GBps": nbytes / (ms * 1e-3) / 1e9}
         # one pass with the scale known in advance (here: the one just computed)
-        _, per = time_launches(lambda: binding.rotate_quant_bf16_prescaled(x, sc, out=out, stream=stream),
-                               steps, warmup, stream)
-        pms = sum(per) / len(per)
+        pms = time_batched(lambda: binding.rotate_quant_bf16_prescaled(x, sc, out=out, stream=stream), steps,
+                           warmup, stream)
         pre[name] = {"kernel_ms_avg": pms, "achieved_GBps": nbytes / (pms * 1e-3) / 1e9}
         del x, out
     # what plain streaming reaches on this GPU with the same traffic: torch's own bf16 -> e4m3
     # cast of the Q-shaped tensor (read 2 bytes, write 1 byte per element, no rotation)
     x = torch.randn((w.B, w.S, w.Hq, w.d_qk), generator=g, device=dev, dtype=torch.float32).to(torch.bfloat16)
     z = torch.empty(x.shape, dtype=torch.float8_e4m3fn, device=dev)
-    _, per = time_launches(lambda: z.copy_(x), steps, warmup, stream)
-    cast_ms = sum(per) / len(per)
+    cast_ms = time_batched(lambda: z.copy_(x), steps, warmup, stream)
     cast_gbps = x.numel() * 3 / (cast_ms * 1e-3) / 1e9
     del x, z
     total_ms = res["q"]["kernel_ms_avg"] + res["k"]["kernel_ms_avg"]
