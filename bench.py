@@ -166,9 +166,10 @@ class PowerClockSampler:
                 "power_source": self.power_file, "clock_source": self.clock_file or self.dpm_file}
 
 
-def measured_traffic(workload, mode):
-    """HBM bytes per launch from the committed rocprofv3 counter summary, or None when the
-    kernel source has changed since those counters were taken (or no summary exists)."""
+def committed_counters(workload, mode):
+    """The committed rocprofv3 counter record (profiles/traffic.json) for this workload and
+    probability path, or None when the kernel source has changed since those counters were
+    taken (or no record exists)."""
     import hashlib
     path = os.path.join(ROOT, "profiles", "traffic.json")
     try:
@@ -180,7 +181,27 @@ def measured_traffic(workload, mode):
         return None
     if t["workload"] != workload or t["p_mode"] != mode:
         return None
-    return t["hbm_read_bytes_per_launch"] + t["hbm_write_bytes_per_launch"]
+    return t
+
+
+def measured_traffic(workload, mode):
+    """HBM bytes per launch from the committed counters, or None (see committed_counters)."""
+    t = committed_counters(workload, mode)
+    return None if t is None else t["hbm_read_bytes_per_launch"] + t["hbm_write_bytes_per_launch"]
+
+
+def valu_roofline(workload, mode):
+    """The vector-side figures of the committed counters: vector instructions per score and lane
+    (MFMA issue excluded) against the pages' budgets, and the vector pipe's share of the kernel's
+    cycles at one wave64 instruction per 4 cycles per SIMD; None when stale (see
+    committed_counters)."""
+    t = committed_counters(workload, mode)
+    if t is None or "valu_per_score" not in t:
+        return None
+    return {"bound": "valu", "valu_instructions_per_score": t["valu_per_score"],
+            "pages_budget_per_score": {"exact": 3.5, "lean": 1.5},
+            "valu_cycles_frac": t["valu_cycles_frac"], "mfma_busy_frac": t["mfma_busy_frac"],
+            "source": t["summary"]}
 
 
 def time_launches(fn, steps, warmup, stream, sampler=None):
@@ -645,7 +666,10 @@ def main():
         "roofline": {"bound": "mfma", "achieved": achieved, "peak": peak, "unit": "TFLOP/s",
                      "frac": achieved / peak,
                      "traffic": measured_traffic(w.name, modes[0]) if args.dtype == "fp8" else None,
-                     "kernel": f"{args.dtype}_causal_fwd", "per_launch_tflop": flops / 1e12},
+                     "kernel": ("fp8_causal_fwd_pair" if modes[0] == "lean" else "fp8_causal_fwd")
+                               if args.dtype == "fp8" else "bf16_causal_fwd",
+                     "per_launch_tflop": flops / 1e12},
+        "valu_roofline": valu_roofline(w.name, modes[0]) if args.dtype == "fp8" else None,
         "paths": paths,
         "rotate_quant": rot,
         "input_study": study,

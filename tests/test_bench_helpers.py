@@ -52,3 +52,25 @@ def test_e4m3_floor_values():
     import bench
     assert abs(bench._e4m3_floor("exact") - 0.0265) < 2e-4
     assert abs(bench._e4m3_floor("lean") - 0.0314) < 2e-4
+
+
+def test_committed_counters_follow_the_kernel_source(tmp_path, monkeypatch):
+    # the counter record is used only while the kernel source it was taken on is unchanged
+    import hashlib
+    import json
+    src = tmp_path / "k.hip"
+    src.write_bytes(b"kernel v1")
+    prof = tmp_path / "profiles"
+    prof.mkdir()
+    rec = {"source": "k.hip", "source_sha256_16": hashlib.sha256(b"kernel v1").hexdigest()[:16],
+           "workload": "gauss32k", "p_mode": "lean", "hbm_read_bytes_per_launch": 10,
+           "hbm_write_bytes_per_launch": 5, "valu_per_score": 3.4, "valu_cycles_frac": 0.5,
+           "mfma_busy_frac": 0.7, "summary": "profiles/x.md"}
+    (prof / "traffic.json").write_text(json.dumps(rec))
+    monkeypatch.setattr(bench, "ROOT", str(tmp_path))
+    assert bench.measured_traffic("gauss32k", "lean") == 15
+    assert bench.valu_roofline("gauss32k", "lean")["valu_instructions_per_score"] == 3.4
+    assert bench.measured_traffic("gauss32k", "exact") is None
+    src.write_bytes(b"kernel v2")
+    assert bench.measured_traffic("gauss32k", "lean") is None
+    assert bench.valu_roofline("gauss32k", "lean") is None
