@@ -166,18 +166,29 @@ class PowerClockSampler:
                 "power_source": self.power_file, "clock_source": self.clock_file or self.dpm_file}
 
 
+def sources_sha16(paths):
+    """First 16 hex digits of the sha256 of the concatenated files (paths relative to the repo)."""
+    import hashlib
+    h = hashlib.sha256()
+    for p in paths:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
 def committed_counters(workload, mode):
     """The committed rocprofv3 counter record (profiles/traffic.json) for this workload and
-    probability path, or None when the kernel source has changed since those counters were
-    taken (or no record exists)."""
-    import hashlib
+    probability path, or None when the kernel's code has changed since those counters were
+    taken (or no record exists).  The record names the files that make the kernel (its
+    source, the headers it includes, the build script with its compiler flags) and the
+    sha256 of their concatenation."""
     path = os.path.join(ROOT, "profiles", "traffic.json")
     try:
         t = json.load(open(path))
-        src = open(os.path.join(ROOT, t["source"]), "rb").read()
+        digest = sources_sha16(t.get("sources") or [t["source"]])
     except Exception:
         return None
-    if hashlib.sha256(src).hexdigest()[:16] != t["source_sha256_16"]:
+    if digest != t["source_sha256_16"]:
         return None
     if t["workload"] != workload or t["p_mode"] != mode:
         return None

@@ -2,7 +2,8 @@
 
     python -m fp8_causal_prefill_tiled_amd.build [--jobs N]
 
-Compiles every source under csrc/ with hipcc for gfx950 and links them into
+Compiles every source under csrc/ with hipcc for gfx950 (the FP8 exponential-path
+source once per head dimension) and links them into
 fp8_causal_prefill_tiled_amd/libattnfwd.so.  Always rebuilds.
 """
 import argparse
@@ -17,8 +18,19 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libattnfwd.so")
-SOURCES = ["api.cpp", "attn_fwd_fp8.hip", "attn_fwd_bf16.hip", "rotate_quant.hip"]
+SOURCES = ["api.cpp", "attn_fwd_fp8.hip", "attn_fwd_fp8_pair.hip", "attn_fwd_bf16.hip", "rotate_quant.hip"]
 ARCH = "gfx950"
+# Compilation units: (object name, source, preprocessor definitions).  The FP8
+# exponential-path source is built once per head dimension, each build with its
+# own code-generation options (see kernel_flags).
+UNITS = [
+    ("api.cpp.o", "api.cpp", {}),
+    ("attn_fwd_fp8_d128.hip.o", "attn_fwd_fp8.hip", {"FP8_EXP_DQK": "128"}),
+    ("attn_fwd_fp8_d192.hip.o", "attn_fwd_fp8.hip", {"FP8_EXP_DQK": "192"}),
+    ("attn_fwd_fp8_pair.hip.o", "attn_fwd_fp8_pair.hip", {}),
+    ("attn_fwd_bf16.hip.o", "attn_fwd_bf16.hip", {}),
+    ("rotate_quant.hip.o", "rotate_quant.hip", {}),
+]
 
 
 def hipcc():
@@ -38,22 +50,34 @@ def common_flags():
     ]
 
 
-def kernel_flags(src):
+def kernel_flags(src, defines=None):
     # Kernel sources only (never the host-side argument checks in api.cpp, whose
     # isfinite() tests must see NaN): inputs are finite by contract, so fmaxf
     # lowers to bare v_max3_f32 without NaN quieting.
     flags = ["-fno-honor-nans"] if src.endswith(".hip") else []
-    if src in ("attn_fwd_fp8.hip", "attn_fwd_bf16.hip", "rotate_quant.hip"):
+    if src in ("attn_fwd_fp8.hip", "attn_fwd_fp8_pair.hip", "attn_fwd_bf16.hip", "rotate_quant.hip"):
         # all matrix results in VGPRs: the score MFMAs' are read directly by the
         # probability code, the P.V accumulators' inline-asm MFMA ties them there, and
         # the rotation's products feed vector butterflies
         flags += ["-mllvm", "-amdgpu-mfma-vgpr-form"]
+    dqk = (defines or {}).get("FP8_EXP_DQK")
+    if src in ("attn_fwd_fp8_pair.hip", "attn_fwd_bf16.hip") or (src == "attn_fwd_fp8.hip" and dqk == "192"):
+        # The two wave groups branch on a wave-uniform index into loops of their own.
+        # Structurized as a divergent if/else, the first group's path falls through into
+        # the second's entry, so everything the second group needs on entry stays live
+        # across the first group's whole loop and is spilled; left as a plain uniform
+        # branch, the two paths share no live ranges.  Not for the d_qk = 128 build of
+        # attn_fwd_fp8.hip: that kernel has no spills either way and measured 7% slower
+        # with it (same loop code, twice the wave wait cycles).
+        flags += ["-mllvm", "-structurizecfg-skip-uniform-regions"]
+    flags += [f"-D{k}={v}" for k, v in (defines or {}).items()]
     return flags
 
 
-def compile_one(src):
-    obj = os.path.join(BUILD, os.path.basename(src) + ".o")
-    cmd = [hipcc()] + common_flags() + kernel_flags(src) + ["-c", os.path.join(CSRC, src), "-o", obj]
+def compile_one(unit):
+    name, src, defines = unit
+    obj = os.path.join(BUILD, name)
+    cmd = [hipcc()] + common_flags() + kernel_flags(src, defines) + ["-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"compile failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
@@ -62,9 +86,9 @@ def compile_one(src):
 
 def build(jobs=None, verbose=False):
     os.makedirs(BUILD, exist_ok=True)
-    jobs = jobs or min(len(SOURCES), max(1, os.cpu_count() or 1))
+    jobs = jobs or min(len(UNITS), max(1, os.cpu_count() or 1))
     with ThreadPoolExecutor(max_workers=jobs) as ex:
-        objs = list(ex.map(compile_one, SOURCES))
+        objs = list(ex.map(compile_one, UNITS))
     tmp = LIB + ".tmp"
     cmd = [hipcc()] + common_flags() + ["-shared", "-o", tmp] + objs
     r = subprocess.run(cmd, capture_output=True, text=True)

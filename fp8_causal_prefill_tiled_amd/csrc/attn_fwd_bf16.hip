@@ -91,7 +91,6 @@ __global__ void __launch_bounds__(512) bf16_causal_fwd(Bf16Params a) {
     constexpr int BM = 256;                       // query rows per workgroup
     constexpr int KPT = T::K_CHUNKS / NT;         // K chunks staged per G0 thread
     constexpr int VPT = T::V_CHUNKS / NT;         // V chunks staged per G1 thread
-    constexpr int SPT = KPT > VPT ? KPT : VPT;
     static_assert(T::K_CHUNKS % NT == 0 && T::V_CHUNKS % NT == 0, "staging split");
 
     __shared__ __attribute__((aligned(16))) uint8_t smem_raw[T::LDS_BYTES];
@@ -172,7 +171,15 @@ __global__ void __launch_bounds__(512) bf16_causal_fwd(Bf16Params a) {
     constexpr int K_TPR = (DQK / 8) % 16 == 0 ? 16 : 8;   // K threads per row
     constexpr int K_CG = DQK / 8 / K_TPR;                  // chunk groups per K row
     static_assert(K_CG * (KB / (NT / K_TPR)) == KPT && (NT / 16) * 4 == KB && VPT == 4, "staging split");
-    i32x4 st[SPT];
+    // Staging registers: one array when both groups stage as many chunks, one per group
+    // when the counts differ.  The compiler merges the groups' loops when their shapes
+    // allow it: one shared array with two counts becomes one loop of run-time length, and
+    // two arrays with one count one loop over a selected array, both indexed in scratch.
+    i32x4 stk[KPT], stv_own[KPT == VPT ? 1 : VPT];
+    auto stv = [&](int i) -> i32x4& {
+        if constexpr (KPT == VPT) return stk[i];
+        else return stv_own[i];
+    };
     int g_base, s_base, g_step;
     {
         const int tpr = grp == 0 ? K_TPR : 16;
@@ -197,11 +204,11 @@ __global__ void __launch_bounds__(512) bf16_causal_fwd(Bf16Params a) {
             const auto r = buffer_rsrc(kbase + (int64_t)j * KB * k_row, rows * k_row);
 #pragma unroll
             for (int i = 0; i < KPT; ++i)
-                st[i] = buffer_load16(r, g_base + (i / K_CG) * g_step + 16 * K_TPR * (i % K_CG));
+                stk[i] = buffer_load16(r, g_base + (i / K_CG) * g_step + 16 * K_TPR * (i % K_CG));
         } else {
             const auto r = buffer_rsrc(vbase + (int64_t)j * KB * v_row, rows * v_row);
 #pragma unroll
-            for (int i = 0; i < VPT; ++i) st[i] = buffer_load16(r, g_base + i * g_step);
+            for (int i = 0; i < VPT; ++i) stv(i) = buffer_load16(r, g_base + i * g_step);
         }
     };
     auto lstore = [&](int j) {   // G0: K slot j%2, G1: V slot j%2
@@ -209,11 +216,11 @@ __global__ void __launch_bounds__(512) bf16_causal_fwd(Bf16Params a) {
             ATTN_LDS uint8_t* base = smem + s_base + (j & 1) * T::K_BYTES;
 #pragma unroll
             for (int i = 0; i < KPT; ++i)
-                lds_store16(base + (i / K_CG) * (NT / K_TPR) * T::K_STRIDE + 16 * K_TPR * (i % K_CG), st[i]);
+                lds_store16(base + (i / K_CG) * (NT / K_TPR) * T::K_STRIDE + 16 * K_TPR * (i % K_CG), stk[i]);
         } else {
             ATTN_LDS uint8_t* base = smem + s_base + (j & 1) * T::V_BYTES;
 #pragma unroll
-            for (int i = 0; i < VPT; ++i) lds_store16(base + i * 16 * 256, st[i]);
+            for (int i = 0; i < VPT; ++i) lds_store16(base + i * 16 * 256, stv(i));
         }
     };
 

@@ -34,7 +34,16 @@ struct Problem {
     const float* dv;
 };
 
-hipError_t launch_fp8(const Problem& p);
+// FP8 attention by probability mode and head dimension, each in a translation unit
+// of its own: Lean P (p_mode 1) in attn_fwd_fp8_pair.hip, the exponential path in
+// the two builds of attn_fwd_fp8.hip.
+hipError_t launch_fp8_lean(const Problem& p);
+hipError_t launch_fp8_exp_d128(const Problem& p);
+hipError_t launch_fp8_exp_d192(const Problem& p);
+inline hipError_t launch_fp8(const Problem& p) {
+    if (p.p_mode == 1) return launch_fp8_lean(p);
+    return p.d_qk == 192 ? launch_fp8_exp_d192(p) : launch_fp8_exp_d128(p);
+}
 hipError_t launch_bf16(const Problem& p);
 // Hadamard rotation + per-tensor e4m3 quantisation of n_el bf16 values (rows of
 // d elements); scale points to one device float.

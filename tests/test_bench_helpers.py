@@ -74,3 +74,12 @@ def test_committed_counters_follow_the_kernel_source(tmp_path, monkeypatch):
     src.write_bytes(b"kernel v2")
     assert bench.measured_traffic("gauss32k", "lean") is None
     assert bench.valu_roofline("gauss32k", "lean") is None
+    # a record over several files (kernel source, headers, build flags) follows each of them
+    hdr = tmp_path / "k.h"
+    hdr.write_bytes(b"header v1")
+    rec["sources"] = ["k.hip", "k.h"]
+    rec["source_sha256_16"] = hashlib.sha256(b"kernel v2" + b"header v1").hexdigest()[:16]
+    (prof / "traffic.json").write_text(json.dumps(rec))
+    assert bench.measured_traffic("gauss32k", "lean") == 15
+    hdr.write_bytes(b"header v2")
+    assert bench.measured_traffic("gauss32k", "lean") is None
