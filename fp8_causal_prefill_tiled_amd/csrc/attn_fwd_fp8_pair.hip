@@ -208,23 +208,33 @@ __global__ void __launch_bounds__(512) fp8_causal_fwd_pair(Fp8Params a) {
         for (int r = 1; r < 16; ++r)
 #pragma unroll
             for (int bl = 0; bl < NB; ++bl) mx[bl] = fmaxf(fmaxf(mx[bl], sc[bl][0][r]), sc[bl][1][r]);
-#pragma unroll
-        for (int bl = 0; bl < NB; ++bl) {
-            mx[bl] = pair_max(mx[bl]);
-            M[bl] = fmaxf(ceilf(mx[bl] * sc_c), -1.0e30f);  // floor: rows with no visible key here
+        // Block exponents.  Lane l holds the maximum of 32 of a block's keys for query l%32;
+        // the other 32 are in lane l^32.  One v_permlane32_swap of the two blocks' maxima
+        // puts both halves of block 0 into lanes 0-31 and both halves of block 1 into
+        // lanes 32-63, so one max and one exponent computation serve both blocks, and a
+        // second swap hands each lane the exponents of both.
+        static_assert(NB == 2, "the exponent exchange pairs the two blocks of a pair");
+        {
+            const auto r = __builtin_amdgcn_permlane32_swap(__float_as_int(mx[0]), __float_as_int(mx[1]), false, false);
+            const float t = fmaxf(__int_as_float(r[0]), __int_as_float(r[1]));
+            // floor: rows with no visible key in the block
+            const int e = __float_as_int(fmaxf(ceilf(t * sc_c), -1.0e30f));
+            const auto m = __builtin_amdgcn_permlane32_swap(e, e, false, false);
+            M[0] = __int_as_float(m[0]);
+            M[1] = __int_as_float(m[1]);
         }
-        float Mmax = M[0];
-#pragma unroll
-        for (int bl = 1; bl < NB; ++bl) Mmax = fmaxf(Mmax, M[bl]);
+        const float Mmax = fmaxf(M[0], M[1]);
         const bool need = Mmax > ref + kRefSlack;
         const float nref = need ? Mmax : ref;
+        // E8M0 byte of 2^(M-8-nref), exponent clamped to [-127, 127]: all terms are integers
+        // in float (or the -1e30 floor), so the sums are exact and one median and one
+        // conversion give it
+        const float sbase = 119.0f - nref;
         float bias[NB];
 #pragma unroll
         for (int bl = 0; bl < NB; ++bl) {
             bias[bl] = PMODE == 0 ? 8.0f - M[bl] : 120.0f - 8.0f * M[bl];
-            // E8M0 byte of 2^(M-8-nref), exponent clamped to [-127, 127]: all terms are
-            // integers in float, so one median and one conversion give it exactly
-            sb[bl] = (int)__builtin_amdgcn_fmed3f(M[bl] - nref + 119.0f, 0.0f, 254.0f);
+            sb[bl] = (int)__builtin_amdgcn_fmed3f(M[bl] + sbase, 0.0f, 254.0f);
         }
         // probability bytes: byte e of all 16 words, then byte e + 1, ... (each word packs its
         // four bytes in sequence; stepping through the words keeps those chains apart)
