@@ -254,20 +254,26 @@ __global__ void __launch_bounds__(512) fp8_causal_fwd_pair(Fp8Params a) {
                     pw[bl][q4] = __builtin_amdgcn_cvt_pk_fp8_f32(p2, p3, wd, true);
                 }
         } else {
+            // every multiply-add first, in place over the scores (all independent), then the
+            // byte conversions byte-major over the 16 words: each conversion's word was last
+            // written 16 conversions earlier, its operand 64 instructions earlier
 #pragma unroll
-            for (int g = 0; g < 8; g += 2) {   // two words of each block at a time
+            for (int h = 0; h < 2; ++h)
 #pragma unroll
-                for (int e = 0; e < 4; ++e)
+                for (int r = 0; r < 16; ++r)
 #pragma unroll
-                    for (int q4 = g; q4 < g + 2; ++q4)
+                    for (int bl = 0; bl < NB; ++bl) sc[bl][h][r] = fmaf(sc[bl][h][r], sc_a8, bias[bl]);
+            __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-                        for (int bl = 0; bl < NB; ++bl) {
-                            const f32x16& x = q4 < 4 ? sc[bl][0] : sc[bl][1];
-                            const float y = fmaf(x[4 * (q4 & 3) + e], sc_a8, bias[bl]);
-                            pw[bl][q4] = (int)__builtin_amdgcn_cvt_pk_u8_f32(y, e, e == 0 ? 0u : (unsigned)pw[bl][q4]);
-                        }
-                __builtin_amdgcn_sched_barrier(0);
-            }
+            for (int e = 0; e < 4; ++e)
+#pragma unroll
+                for (int q4 = 0; q4 < 8; ++q4)
+#pragma unroll
+                    for (int bl = 0; bl < NB; ++bl) {
+                        const float y = (q4 < 4 ? sc[bl][0] : sc[bl][1])[4 * (q4 & 3) + e];
+                        pw[bl][q4] = (int)__builtin_amdgcn_cvt_pk_u8_f32(y, e, e == 0 ? 0u : (unsigned)pw[bl][q4]);
+                    }
+            __builtin_amdgcn_sched_barrier(0);
         }
 #pragma unroll
         for (int bl = 0; bl < NB; ++bl)
