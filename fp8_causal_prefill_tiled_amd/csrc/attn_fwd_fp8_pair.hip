@@ -46,8 +46,9 @@ __global__ void __launch_bounds__(512) fp8_causal_fwd_pair(Fp8Params a) {
     const float sc_c = scl.c, sc_a8 = scl.a8;
     const int k_row = a.Hkv * DQK;                // bytes between consecutive keys
     const int v_row = a.Hkv * 128;
-    const uint8_t* kbase = a.k + u.tok0k * k_row + (int64_t)u.g * DQK;
-    const uint8_t* vbase = a.v + u.tok0k * v_row + (int64_t)u.g * 128;
+    // wave-uniform bases, so that the per-block staging addresses are scalar arithmetic
+    const uint8_t* kbase = uniform_ptr(a.k + u.tok0k * k_row + (int64_t)u.g * DQK);
+    const uint8_t* vbase = uniform_ptr(a.v + u.tok0k * v_row + (int64_t)u.g * 128);
     i32x8 qr[T::NKK];
     load_q<DQK>(a, u, qabs, hh, qr);
 

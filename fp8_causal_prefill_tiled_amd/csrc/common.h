@@ -53,6 +53,15 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, 
                                              __builtin_amdgcn_readfirstlane(bytes), 0x00020000);
 }
 
+// A wave-uniform pointer read from the first lane, so that it and the per-block addresses
+// derived from it by uniform offsets are scalar values (no per-block readfirstlane).
+__device__ __forceinline__ const uint8_t* uniform_ptr(const uint8_t* p) {
+    const unsigned long long x = (unsigned long long)p;
+    const unsigned long long lo = (unsigned)__builtin_amdgcn_readfirstlane((int)x);
+    const unsigned long long hi = (unsigned)__builtin_amdgcn_readfirstlane((int)(x >> 32));
+    return (const uint8_t*)(lo | (hi << 32));
+}
+
 __device__ __forceinline__ i32x4 buffer_load16(__amdgpu_buffer_rsrc_t r, int offset) {
     return __builtin_amdgcn_raw_buffer_load_b128(r, offset, 0, 0);
 }
