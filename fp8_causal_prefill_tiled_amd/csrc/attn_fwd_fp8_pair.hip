@@ -190,9 +190,21 @@ __global__ void __launch_bounds__(512) fp8_causal_fwd_pair(Fp8Params a) {
         // formula leaves a block that lies wholly inside the visible range unchanged
         if (NB * p + NB - 1 >= jdiag) {
             const int qlim = CAUSAL ? min(qabs + qoff, Sk - 1) : Sk - 1;
+            // the same bound for the wave's first and last query (qlim grows with the
+            // query): a block every lane sees whole, or none of, needs no per-key test
+            const int qw = __builtin_amdgcn_readfirstlane(q0 + 32 * w);
+            const int qlo = CAUSAL ? min(qw + qoff, Sk - 1) : Sk - 1;
+            const int qhi = CAUSAL ? min(qw + 31 + qoff, Sk - 1) : Sk - 1;
 #pragma unroll
             for (int bl = 0; bl < NB; ++bl) {
-                const int lim = qlim - (NB * p + bl) * KB - 4 * hh;
+                const int kb0 = (NB * p + bl) * KB;
+                if (qlo - kb0 - 4 >= 32 + 27) continue;   // every key visible to every lane
+                if (qhi - kb0 < 0) {                       // no key visible to any lane
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) sc[bl][0][r] = sc[bl][1][r] = -INFINITY;
+                    continue;
+                }
+                const int lim = qlim - kb0 - 4 * hh;
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
                     const int off = 8 * (r >> 2) + (r & 3);
