@@ -53,6 +53,38 @@ def test_ragged_and_gqa_full_tensor(shape, mode):
     assert np.array_equal(got[:, 0].astype(np.float32), row0_expected_fp8(d)[:, np.arange(Hq) // (Hq // Hkv)])
 
 
+# More than 32 query heads in all with K/V heads in multiples of 8: the workgroups run in
+# bands of tiles of one query head, the heads of one K/V head on one XCD (with GQA, the
+# query heads of a K/V head adjacent); every (tile, head) must be computed once.
+@pytest.mark.parametrize("mode", MODES)
+@pytest.mark.parametrize("shape", [(2, 32, 4, 300, 128), (1, 40, 8, 300, 192), (1, 64, 64, 140, 128)])
+def test_banded_tile_order_full_tensor(shape, mode):
+    B, Hq, Hkv, S, dqk = shape
+    w = custom(B, Hq, Hkv, S, dqk)
+    d = W.make_fp8(w, seed=901 + S)
+    got = gpu_select(run_fp8(d, mode))
+    emu, ref = oracle_fp8(d, mode)
+    check_fp8(got, emu, ref, f"{w.name} {mode}", d=d, mode=mode)
+    assert np.array_equal(got[:, 0].astype(np.float32), row0_expected_fp8(d)[:, np.arange(Hq) // (Hq // Hkv)])
+
+
+@pytest.mark.parametrize("mode", MODES)
+def test_banded_tile_order_full_band_sampled(mode):
+    # 33 query tiles per head: one full band of 32 tiles and a partial band of one
+    B, Hq, Hkv, S = 2, 32, 8, 32 * 256 + 100
+    w = custom(B, Hq, Hkv, S, 128)
+    d = W.make_fp8(w, seed=4242)
+    out = run_fp8(d, mode)
+    rows = np.unique(np.concatenate([np.arange(0, S, 97), np.arange(S - 300, S)]))
+    heads = [0, 5, 17, 31]
+    got = gpu_select(out, heads=heads, rows=rows)
+    assert bool(torch.isfinite(out).all())
+    del out
+    emu, ref = oracle_fp8(d, mode, heads=heads, rows=rows)
+    check_fp8(got, emu, ref, f"{w.name} {mode} (rows={len(rows)}, heads={heads})", rows=rows, d=d, mode=mode,
+              heads=heads)
+
+
 @pytest.mark.parametrize("mode", MODES)
 def test_zero_query_is_prefix_mean(mode):
     w = custom(1, 2, 2, 300, 128)
