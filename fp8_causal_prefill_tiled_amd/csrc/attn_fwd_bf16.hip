@@ -103,8 +103,8 @@ __global__ void __launch_bounds__(512) bf16_causal_fwd(Bf16Params a) {
     const int tg = tid & (NT - 1);                            // thread index in its group
     const int BH = a.B * a.Hq;
     const int L = blockIdx.x;
-    const int tile = a.n_tiles - 1 - L / BH;      // heaviest (longest causal prefix) tiles first when causal
-    const int bh = L % BH;                        // consecutive blocks: consecutive heads (XCD spread)
+    int tile, bh;
+    tile_of(L, BH, a.Hq / a.Hkv, a.n_tiles, tile, bh);
     const int b = bh / a.Hq;
     const int h = bh - b * a.Hq;
     const int g = h / (a.Hq / a.Hkv);

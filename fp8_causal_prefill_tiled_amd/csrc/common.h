@@ -62,6 +62,39 @@ __device__ __forceinline__ const uint8_t* uniform_ptr(const uint8_t* p) {
     return (const uint8_t*)(lo | (hi << 32));
 }
 
+// Query tile and (sequence, query head) index bh of workgroup L, in a grid of nt tiles
+// (256 queries each) for each of BH query heads, ratio query heads per K/V head.
+// Workgroups go to the 8 XCDs round-robin by index.  With more than 4 query heads per
+// XCD, a tile-major order would run only a few tiles of each head together on an XCD,
+// each streaming its own K/V prefix through that XCD's L2.  Instead XCD x then runs the
+// query heads of the K/V heads g = x (mod 8) (so each K/V head is read through one
+// L2), in bands of up to 32 tiles of one query head, the heads of one K/V head
+// adjacent, heaviest band first: the workgroups running together on an XCD share one
+// K/V prefix.  Otherwise (and when K/V heads do not divide over the XCDs) the order is
+// tile-major, heaviest (longest causal prefix) tiles first.
+__device__ __forceinline__ void tile_of(int L, int BH, int ratio, int nt, int& tile, int& bh) {
+    if (BH > 32 && (BH / ratio) % 8 == 0) {
+        constexpr int G = 32;                   // about one workgroup per CU of an XCD
+        const int x = L & 7, idx = L >> 3, nh = BH >> 3;
+        const int fb = nt / G;                  // full bands
+        int k, t;
+        if (idx < fb * G * nh) {
+            const int band = idx / (G * nh), rem = idx - band * (G * nh);
+            k = rem / G;
+            t = band * G + (rem - k * G);
+        } else {
+            const int r = nt - fb * G, rem = idx - fb * G * nh;   // the last, partial band
+            k = rem / r;
+            t = fb * G + (rem - k * r);
+        }
+        tile = nt - 1 - t;
+        bh = (x + 8 * (k / ratio)) * ratio + k % ratio;
+    } else {
+        tile = nt - 1 - L / BH;
+        bh = L % BH;
+    }
+}
+
 __device__ __forceinline__ i32x4 buffer_load16(__amdgpu_buffer_rsrc_t r, int offset) {
     return __builtin_amdgcn_raw_buffer_load_b128(r, offset, 0, 0);
 }

@@ -113,36 +113,8 @@ __device__ __forceinline__ bool work_of(const Fp8Params& a, Work& u) {
     constexpr int BM = 256;
     const int BH = a.B * a.Hq;
     const int L = blockIdx.x;
-    const int ratio = a.Hq / a.Hkv;             // query heads per K/V head
     int tile, bh;
-    if (BH > 32 && (BH / ratio) % 8 == 0) {
-        // Workgroups go to the 8 XCDs round-robin by index.  With more than 4 query heads
-        // per XCD, the tile-major order below would run only a few tiles of each head
-        // together on an XCD, each streaming its own K/V prefix through that XCD's L2.
-        // Instead XCD x runs the query heads of the K/V heads g = x (mod 8) (so each K/V
-        // head is read through one L2), in bands of up to G tiles of one query head, the
-        // heads of one K/V head adjacent, heaviest band first: the workgroups running
-        // together on an XCD share one K/V prefix.
-        constexpr int G = 32;                   // about one workgroup per CU of an XCD
-        const int x = L & 7, idx = L >> 3, nh = BH >> 3, nt = a.n_tiles;
-        const int fb = nt / G;                  // full bands
-        int k, t;
-        if (idx < fb * G * nh) {
-            const int band = idx / (G * nh), rem = idx - band * (G * nh);
-            k = rem / G;
-            t = band * G + (rem - k * G);
-        } else {
-            const int r = nt - fb * G, rem = idx - fb * G * nh;   // the last, partial band
-            k = rem / r;
-            t = fb * G + (rem - k * r);
-        }
-        tile = nt - 1 - t;
-        bh = (x + 8 * (k / ratio)) * ratio + k % ratio;
-    } else {
-        // tile-major, heaviest tiles first
-        tile = a.n_tiles - 1 - L / BH;
-        bh = L % BH;
-    }
+    tile_of(L, BH, a.Hq / a.Hkv, a.n_tiles, tile, bh);
     u.b = bh / a.Hq;
     u.h = bh - u.b * a.Hq;
     u.g = u.h / (a.Hq / a.Hkv);

@@ -203,7 +203,9 @@ def test_north_star_fixed_fp64_bar(name, mode):
 # ----------------------------------------------------------------------------- BF16
 
 @pytest.mark.parametrize("shape", [(1, 2, 2, 256, 128), (2, 4, 2, 129, 128), (1, 4, 1, 333, 192),
-                                   (1, 2, 2, 1, 128), (1, 2, 2, 65, 192)])
+                                   (1, 2, 2, 1, 128), (1, 2, 2, 65, 192),
+                                   # more than 32 query heads, K/V heads in multiples of 8: banded order
+                                   (2, 32, 4, 300, 128), (1, 40, 8, 300, 192)])
 def test_bf16_full_tensor(shape):
     B, Hq, Hkv, S, dqk = shape
     d = W.make_bf16(custom(B, Hq, Hkv, S, dqk), seed=31 + S)
