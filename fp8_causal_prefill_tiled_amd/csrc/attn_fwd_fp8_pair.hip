@@ -141,9 +141,6 @@ __global__ void __launch_bounds__(512) fp8_causal_fwd_pair(Fp8Params a) {
     for (int dt = 0; dt < 4; ++dt) o[dt] = f32x16{0};
     f32x16 lsum = f32x16{0};
     float ref = -INFINITY;
-    // e4m3 1.0 in every byte, the A operand of the row-sum MFMAs: 32 bytes of LDS that
-    // every lane reads (a broadcast read) at the start of each MFMA phase.
-    if (tid < 2) lds_store16(smem + T::OFF_ONES + 16 * tid, i32x4{0x38383838, 0x38383838, 0x38383838, 0x38383838});
     // The A-side E8M0 scale of the P.V MFMAs (127 = 2^0), set once here under a
     // full EXEC mask: matrix instructions read every lane's scale byte whatever
     // EXEC is, so the constant must never be materialised inside divergent code.
@@ -327,7 +324,10 @@ __global__ void __launch_bounds__(512) fp8_causal_fwd_pair(Fp8Params a) {
             const int k = i - NPV, jb = NB * (p + 1) + k / NS, ks = k % NS;
             return kread(jb & (NSLOT - 1), ks & 1, ks >> 1);
         };
-        const i32x8 ones = read32(smem + T::OFF_ONES);
+        // e4m3 1.0 in every byte, the A operand of the row-sum MFMAs: a constant, so it stays
+        // in registers across the loop (read from LDS it cost two reads and a wait per phase)
+        const i32x8 ones = i32x8{0x38383838, 0x38383838, 0x38383838, 0x38383838,
+                                 0x38383838, 0x38383838, 0x38383838, 0x38383838};
         constexpr int PD = 2;            // operands read this many MFMAs ahead
         i32x8 opb[PD + 1];
 #pragma unroll

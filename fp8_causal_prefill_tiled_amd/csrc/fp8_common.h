@@ -47,8 +47,7 @@ struct PairTile {
     static constexpr int NSLOT = 2 * NB;
     static constexpr int OFF_VT = NSLOT * K_BYTES;
     static constexpr int OFF_VS = OFF_VT + NSLOT * VT_BYTES;
-    static constexpr int OFF_ONES = OFF_VS + NSLOT * V_BYTES;   // 32 bytes of e4m3 1.0
-    static constexpr int LDS_BYTES = OFF_ONES + 32;
+    static constexpr int LDS_BYTES = OFF_VS + NSLOT * V_BYTES;
 
 };
 
