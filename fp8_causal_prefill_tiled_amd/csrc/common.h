@@ -72,7 +72,7 @@ __device__ __forceinline__ const uint8_t* uniform_ptr(const uint8_t* p) {
 // adjacent, heaviest band first: the workgroups running together on an XCD share one
 // K/V prefix.  Otherwise (and when K/V heads do not divide over the XCDs) the order is
 // tile-major, heaviest (longest causal prefix) tiles first.
-__device__ __forceinline__ void tile_of(int L, int BH, int ratio, int nt, int& tile, int& bh) {
+__host__ __device__ __forceinline__ void tile_of(int L, int BH, int ratio, int nt, int& tile, int& bh) {
     if (BH > 32 && (BH / ratio) % 8 == 0) {
         constexpr int G = 32;                   // about one workgroup per CU of an XCD
         const int x = L & 7, idx = L >> 3, nh = BH >> 3;
