@@ -43,7 +43,21 @@ __global__ void __launch_bounds__(512) fp8_causal_fwd_pair(Fp8Params a) {
     const int hh = lane >> 5;
     const int qabs = q0 + 32 * w + c;             // query of this lane
     const Scales scl = scales_of<DSCALE>(a);
-    const float sc_c = scl.c, sc_a8 = scl.a8;
+    const float sc_a8 = scl.a8;
+    // Lean P codes as f32 subnormals.  The score MFMAs scale S by 2^-ksh (E8M0 operand
+    // scales, exact), so that m0 = a8 * 2^(ksh-149) is a normal float; then one fused
+    // fma(S', m0, (120 - 8M) * 2^-149) rounds a8 S + 120 - 8M to the subnormal grid, whose
+    // ulp is one code: the result's bit pattern is the integer code, and the output clamp to
+    // [0, 1] sends negative codes (and masked -inf scores) to 0.  This replaces the
+    // float-to-byte conversion of every probability with a quarter as many byte permutes.
+    const int ea8 = (int)((__float_as_uint(sc_a8) >> 23) & 0xff) - 127;   // a8 = 8c > 0, normal
+    const int ksh = PMODE == 1 ? min(max(24 - ea8, 0), 254) : 0;
+    const float sc_c = ldexpf(scl.c, ksh);        // c in units of S' (c * S = sc_c * S')
+    const float sc_m0 = ldexpf(sc_a8, ksh - 149);
+    // E8M0 scale bytes of the score MFMAs, set once under a full EXEC mask like sa below:
+    // byte 0 (K operand) 2^-max(ksh-127, 0), byte 1 (Q operand) 2^-min(ksh, 127)
+    int sks = (127 - max(ksh - 127, 0)) | ((127 - min(ksh, 127)) << 8);
+    asm volatile("" : "+v"(sks));
     const int k_row = a.Hkv * DQK;                // bytes between consecutive keys
     const int v_row = a.Hkv * 128;
     // wave-uniform bases, so that the per-block staging addresses are scalar arithmetic
@@ -170,6 +184,12 @@ __global__ void __launch_bounds__(512) fp8_causal_fwd_pair(Fp8Params a) {
         return i32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
     };
 
+    // S^T += K.Q^T over one d step; on the Lean P path scaled by 2^-ksh (scale bytes in sks)
+    auto score_mfma = [&](const i32x8& kop, const i32x8& qop, const f32x16& acc) {
+        if (PMODE == 1) return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(kop, qop, acc, 0, 0, 0, sks, 1, sks);
+        return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(kop, qop, acc, 0, 0, 0, 0, 0, 0);
+    };
+
     f32x16 sc[NB][2];           // S^T of the next block pair: block bl, keys [0,32) / [32,64)
     i32x8 pv[NB];               // P of the current pair, the B operands of the P.V MFMAs
     int sb[NB];                 // their E8M0 scale bytes
@@ -243,7 +263,8 @@ __global__ void __launch_bounds__(512) fp8_causal_fwd_pair(Fp8Params a) {
         float bias[NB];
 #pragma unroll
         for (int bl = 0; bl < NB; ++bl) {
-            bias[bl] = PMODE == 0 ? 8.0f - M[bl] : 120.0f - 8.0f * M[bl];
+            // Lean P: (120 - 8M) * 2^-149, exact (an integer times the subnormal ulp)
+            bias[bl] = PMODE == 0 ? 8.0f - M[bl] : fmaf(M[bl], -0x1p-146f, 120.0f * 0x1p-149f);
             sb[bl] = (int)__builtin_amdgcn_fmed3f(M[bl] + sbase, 0.0f, 254.0f);
         }
         // probability bytes: byte e of all 16 words, then byte e + 1, ... (each word packs its
@@ -264,25 +285,34 @@ __global__ void __launch_bounds__(512) fp8_causal_fwd_pair(Fp8Params a) {
                     pw[bl][q4] = __builtin_amdgcn_cvt_pk_fp8_f32(p2, p3, wd, true);
                 }
         } else {
-            // every multiply-add first, in place over the scores (all independent), then the
-            // byte conversions byte-major over the 16 words: each conversion's word was last
-            // written 16 conversions earlier, its operand 64 instructions earlier
+            // every clamped multiply-add first, in place over the scores (all independent; the
+            // clamp folds into the FMA), then the codes into words: bytes (c0, c1) and (c2, c3)
+            // of each word into the low halves of two words, then those into one, three byte
+            // permutes per word (written as shifts and ors they are re-associated into four)
 #pragma unroll
             for (int h = 0; h < 2; ++h)
 #pragma unroll
                 for (int r = 0; r < 16; ++r)
 #pragma unroll
-                    for (int bl = 0; bl < NB; ++bl) sc[bl][h][r] = fmaf(sc[bl][h][r], sc_a8, bias[bl]);
+                    for (int bl = 0; bl < NB; ++bl)
+                        sc[bl][h][r] = __builtin_amdgcn_fmed3f(fmaf(sc[bl][h][r], sc_m0, bias[bl]), 0.0f, 1.0f);
             __builtin_amdgcn_sched_barrier(0);
+            auto code = [&](int bl, int q4, int e) {   // code of word q4, byte e, as an integer
+                return __float_as_uint((q4 < 4 ? sc[bl][0] : sc[bl][1])[4 * (q4 & 3) + e]);
+            };
+            unsigned lo2[NB][8], hi2[NB][8];
 #pragma unroll
-            for (int e = 0; e < 4; ++e)
+            for (int q4 = 0; q4 < 8; ++q4)
 #pragma unroll
-                for (int q4 = 0; q4 < 8; ++q4)
+                for (int bl = 0; bl < NB; ++bl) lo2[bl][q4] = __builtin_amdgcn_perm(code(bl, q4, 1), code(bl, q4, 0), 0x0c0c0400u);
 #pragma unroll
-                    for (int bl = 0; bl < NB; ++bl) {
-                        const float y = (q4 < 4 ? sc[bl][0] : sc[bl][1])[4 * (q4 & 3) + e];
-                        pw[bl][q4] = (int)__builtin_amdgcn_cvt_pk_u8_f32(y, e, e == 0 ? 0u : (unsigned)pw[bl][q4]);
-                    }
+            for (int q4 = 0; q4 < 8; ++q4)
+#pragma unroll
+                for (int bl = 0; bl < NB; ++bl) hi2[bl][q4] = __builtin_amdgcn_perm(code(bl, q4, 3), code(bl, q4, 2), 0x0c0c0400u);
+#pragma unroll
+            for (int q4 = 0; q4 < 8; ++q4)
+#pragma unroll
+                for (int bl = 0; bl < NB; ++bl) pw[bl][q4] = (int)__builtin_amdgcn_perm(hi2[bl][q4], lo2[bl][q4], 0x05040100u);
             __builtin_amdgcn_sched_barrier(0);
         }
 #pragma unroll
@@ -343,8 +373,7 @@ __global__ void __launch_bounds__(512) fp8_causal_fwd_pair(Fp8Params a) {
             } else {
                 const int k = i - NPV, bl = k / NS, ks = k % NS;
                 f32x16& sd = sc[bl][ks & 1];
-                sd = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(opb[i % (PD + 1)], qr[ks >> 1],
-                                                                      ks < 2 ? f32x16{0} : sd, 0, 0, 0, 0, 0, 0);
+                sd = score_mfma(opb[i % (PD + 1)], qr[ks >> 1], ks < 2 ? f32x16{0} : sd);
             }
             extra(i);
             __builtin_amdgcn_sched_barrier(0);
@@ -364,8 +393,8 @@ __global__ void __launch_bounds__(512) fp8_causal_fwd_pair(Fp8Params a) {
         f32x16 s0 = f32x16{0}, s1 = f32x16{0};
 #pragma unroll
         for (int kk = 0; kk < T::NKK; ++kk) {
-            s0 = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(kread(bl, 0, kk), qr[kk], s0, 0, 0, 0, 0, 0, 0);
-            s1 = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(kread(bl, 1, kk), qr[kk], s1, 0, 0, 0, 0, 0, 0);
+            s0 = score_mfma(kread(bl, 0, kk), qr[kk], s0);
+            s1 = score_mfma(kread(bl, 1, kk), qr[kk], s1);
         }
         sc[bl][0] = s0;
         sc[bl][1] = s1;

@@ -8,7 +8,10 @@
 * the E8M0 clamp: later blocks that sit more than 127 log2 units below the row's
   reference, so that their scale exponent M - 8 - R falls below the E8M0 range;
 * the last, ragged query tile (S = 557: 45 rows past the last full 256-row tile, every
-  row's visible keys ending inside a block).
+  row's visible keys ending inside a block);
+* per-tensor scales far from the usual amax/448: the Lean P kernel scales the scores by a
+  power of two chosen from a8 = 8c inside its score MFMAs (both E8M0 operand scales for
+  the smallest products q_scale * k_scale), which these cases drive end to end.
 
 Every output row is compared with the emulation (FP8, per-row bars of tests/parity.py) or
 with fp64 attention (BF16).  The premise of each case (the reference moves at every block,
@@ -111,3 +114,26 @@ def test_fp8_last_ragged_tile_rows(dqk, mode):
     tail = np.arange(512, S)
     check_fp8(got[:, tail], emu[:, tail], ref[:, tail], f"last tile d{dqk} {mode}", rows=tail, d=d, mode=mode)
     check_fp8(got, emu, ref, f"all rows d{dqk} {mode}", d=d, mode=mode)
+
+
+@pytest.mark.parametrize("mode", ["exact", "lean"])
+@pytest.mark.parametrize("dqk", [128, 192])
+@pytest.mark.parametrize("log2_qk,dev", [(-112, True), (-96, False), (-60, False), (-60, True)])
+def test_fp8_scale_range(dqk, mode, log2_qk, dev):
+    # q_scale * k_scale = 2^log2_qk with the same codes (the Gaussian draws give about 2^-13):
+    # every score is then ~0 and the weights uniform.  At -112 the Lean P kernel's score shift
+    # spans both E8M0 operand bytes; only device scales reach it (the host entry rejects
+    # c <= 1e-30).  Much larger products give logits of thousands of log2 units, where the
+    # per-row bars' model of the dot product's rounding no longer bounds either path.
+    d = W.make_fp8(W.Workload("scales", 1, 4, 2, 300, dqk, 128), seed=77)
+    d["q_scale"] = d["k_scale"] = 2.0 ** (log2_qk / 2)
+    if dev:
+        sc = [torch.tensor([d[n]], dtype=torch.float32, device="cuda:0") for n in ("q_scale", "k_scale", "v_scale")]
+        q8, k8, v8 = (d[n].to("cuda:0") for n in ("q8", "k8", "v8"))
+        out = binding.attn_fwd_fp8(q8, k8, v8, *sc, p_mode=mode)
+        torch.cuda.synchronize()
+    else:
+        out = run_fp8(d, mode)
+    got = gpu_select(out)
+    emu, ref = oracle_fp8(d, mode)
+    check_fp8(got, emu, ref, f"scales 2^{log2_qk} {'device' if dev else 'host'} d{dqk} {mode}", d=d, mode=mode)
