@@ -79,7 +79,9 @@ __device__ __forceinline__ int v_swz16(int row) { return (row & 3) << 1; }
 
 // acc += A . B on the BF16 matrix cores (32x32x16), the accumulator tied to the
 // destination registers (the builtin may give the result registers of its own
-// and copy it back every iteration).  Results are read only after vacc_settle.
+// and copy it back every iteration).  Results are read only after vacc_settle; the
+// leading s_nop gives a vector write of an operand register just before it the wait
+// states the compiler does not insert around inline asm.
 __device__ __forceinline__ void mfma_bf16_vacc(f32x16& acc, const bf16x8& a, const bf16x8& b) {
     asm("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(acc) : "v"(a), "v"(b));
 }

@@ -23,7 +23,6 @@ template <int DQK, int PMODE, bool CAUSAL, bool LSE, bool VARLEN, bool DSCALE>
 __global__ void __launch_bounds__(512) fp8_causal_fwd_pair(Fp8Params a) {
     using T = PairTile<DQK>;
     constexpr int NT = 256;                       // threads per group
-    constexpr int BM = 256;                       // query rows per workgroup
     constexpr int NB = T::NB;                     // 64-key blocks per iteration
     constexpr int NSLOT = T::NSLOT;
     constexpr int TPT = (128 * 4) / NT;           // V^T chunks of one block built per thread
@@ -35,7 +34,6 @@ __global__ void __launch_bounds__(512) fp8_causal_fwd_pair(Fp8Params a) {
     const int lane = tid & 63;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave index, uniform
     const int grp = w >> 2;                                   // 0: G0, 1: G1
-    const int tg = tid & (NT - 1);                            // thread index in its group
     Work u;
     if (!work_of<CAUSAL, VARLEN>(a, u)) return;
     const int S = u.S, Sk = u.Sk, qoff = u.qoff, q0 = u.q0, nblk = u.nblk, jdiag = u.jdiag;
@@ -160,6 +158,13 @@ __global__ void __launch_bounds__(512) fp8_causal_fwd_pair(Fp8Params a) {
     // EXEC is, so the constant must never be materialised inside divergent code.
     int sa = 127;
     asm volatile("" : "+v"(sa));
+    // e4m3 1.0 in every byte, the A operand of the row-sum MFMAs, kept in registers across the
+    // loop (read from LDS it cost two reads and a wait per phase).  Opaque to the compiler, so
+    // it is never rematerialised by vector moves just ahead of an (inline asm) matrix
+    // instruction that reads it, a hazard the compiler does not see.
+    i32x8 ones = i32x8{0x38383838, 0x38383838, 0x38383838, 0x38383838,
+                       0x38383838, 0x38383838, 0x38383838, 0x38383838};
+    asm volatile("" : "+v"(ones));
 
     auto read32 = [&](const ATTN_LDS uint8_t* p) {
         i32x4 lo = lds_load16(p), hi = lds_load16(p + 16);
@@ -202,7 +207,7 @@ __global__ void __launch_bounds__(512) fp8_causal_fwd_pair(Fp8Params a) {
     // reference moves (by more than kRefSlack), E8M0 scale bytes.  The two blocks'
     // dependency chains (the row maxima, the byte packing of each word) are interleaved:
     // a wave issues a dependent vector instruction more slowly than an independent one.
-    auto valu_phase = [&](int p) {
+    auto valu_phase = [&] [[gnu::always_inline]] (int p) {
         // masks: only pairs that reach the diagonal (or the ragged last block); the
         // formula leaves a block that lies wholly inside the visible range unchanged
         if (NB * p + NB - 1 >= jdiag) {
@@ -343,7 +348,7 @@ __global__ void __launch_bounds__(512) fp8_causal_fwd_pair(Fp8Params a) {
     // else K operand: block (i-NPV)/NS, key half, d step) is read two MFMAs ahead of
     // its use; extra(i) runs after MFMA i: the staging work of the MFMA wave, issued
     // while the matrix pipe is busy.
-    auto mfma_phase = [&](int p, auto&& extra) {
+    auto mfma_phase = [&] [[gnu::always_inline]] (int p, auto&& extra) {
         __builtin_amdgcn_s_setprio(1);   // matrix issue wins arbitration against the partner wave
         auto operand = [&](int i) {
             if (i < NPV) {
@@ -354,10 +359,6 @@ __global__ void __launch_bounds__(512) fp8_causal_fwd_pair(Fp8Params a) {
             const int k = i - NPV, jb = NB * (p + 1) + k / NS, ks = k % NS;
             return kread(jb & (NSLOT - 1), ks & 1, ks >> 1);
         };
-        // e4m3 1.0 in every byte, the A operand of the row-sum MFMAs: a constant, so it stays
-        // in registers across the loop (read from LDS it cost two reads and a wait per phase)
-        const i32x8 ones = i32x8{0x38383838, 0x38383838, 0x38383838, 0x38383838,
-                                 0x38383838, 0x38383838, 0x38383838, 0x38383838};
         constexpr int PD = 2;            // operands read this many MFMAs ahead
         i32x8 opb[PD + 1];
 #pragma unroll
@@ -413,9 +414,13 @@ __global__ void __launch_bounds__(512) fp8_causal_fwd_pair(Fp8Params a) {
     // before the end-of-iteration barrier.  LDS slots: block jb in slot jb % NSLOT,
     // NSLOT = 2*NB.
     const int npair = (nblk + NB - 1) / NB;
+    // The loop is unrolled by two pairs (NSLOT / NB): within each copy every slot index is a
+    // constant, so LDS operand and staging addresses fold into instruction offsets (the
+    // phases are forced inline: called five times, the vector phase would otherwise become
+    // a function call).
+    static_assert(NSLOT == 2 * NB, "two pairs per unrolled iteration cycle through the slots");
     if (grp == 0) {
-        valu_phase(0);
-        for (int p = 0; p < npair; ++p) {
+        auto iter = [&] [[gnu::always_inline]] (int p) {
             mfma_phase(p, [&](int i) {                    // MFMA(p)
                 if (i == 0) transpose_read(NB * (p + 1));
                 if (i == 4) transpose_write(NB * (p + 1));
@@ -423,9 +428,14 @@ __global__ void __launch_bounds__(512) fp8_causal_fwd_pair(Fp8Params a) {
             dload(p + 2);
             valu_phase(p + 1);                            // VALU(p+1)
             vmem_lds_sync();
+        };
+        valu_phase(0);
+        for (int pp = 0; 2 * pp < npair; ++pp) {
+            iter(2 * pp);
+            if (2 * pp + 1 < npair) iter(2 * pp + 1);
         }
     } else {
-        for (int p = 0; p < npair; ++p) {
+        auto iter = [&] [[gnu::always_inline]] (int p) {
             dload(p + 2);
             valu_phase(p);                                // VALU(p)
             mfma_phase(p, [&](int i) {                    // MFMA(p)
@@ -433,6 +443,10 @@ __global__ void __launch_bounds__(512) fp8_causal_fwd_pair(Fp8Params a) {
                 if (i == 4) transpose_write(NB * (p + 1) + 1);
             });
             vmem_lds_sync();
+        };
+        for (int pp = 0; 2 * pp < npair; ++pp) {
+            iter(2 * pp);
+            if (2 * pp + 1 < npair) iter(2 * pp + 1);
         }
     }
     // The matrix instructions ignore EXEC: settling the accumulators here also keeps

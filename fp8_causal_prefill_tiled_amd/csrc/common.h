@@ -127,7 +127,12 @@ __device__ __forceinline__ i16x8 i16x8_cat(i16x4 a, i16x4 b) {
 // acc += A . B on the FP8 matrix cores (32x32x64, e4m3 operands) with per-lane E8M0
 // scales: A's byte from scale_a, B's from scale_b.  The accumulator is tied to the
 // destination registers (the builtin in VGPR form may give the result registers of
-// its own and copy it back on every iteration).
+// its own and copy it back on every iteration, and, being free of side effects, is
+// moved across the phase structure).  The compiler inserts no wait states around an
+// instruction it cannot see: operands must not be written by a vector instruction just
+// ahead of it (callers keep constants opaque so they are not rematerialised there; a
+// test scans the built code for that hazard), and results are read only after
+// vacc_settle.
 __device__ __forceinline__ void mfma_f8_scaled_vacc(f32x16& acc, const i32x8& a, const i32x8& b, int scale_a,
                                                     int scale_b) {
     asm("v_mfma_scale_f32_32x32x64_f8f6f4 %0, %1, %2, %0, %3, %4 op_sel_hi:[0,0,0]"
