@@ -141,10 +141,13 @@ __device__ __forceinline__ void mfma_f8_scaled_vacc(f32x16& acc, const i32x8& a,
 }
 
 // Before any other instruction touches accumulators written by mfma_f8_scaled_vacc:
-// a 16-pass MFMA needs independent cycles before its result may be read, which the
-// compiler does not insert for inline asm; 24 wait states cover it.  Being volatile
-// and tied to every accumulator, this also keeps all of those MFMAs in uniform
-// control flow ahead of it.
+// an XDL MFMA's result may be read or overwritten by a non-matrix instruction only a
+// number of wait states after it that grows with its passes (the CDNA3/CDNA4 ISA
+// guides' table of required independent instructions).  The compiler does not insert
+// them for inline asm; for its own builtins on gfx950 it inserts 20 after the 16-pass
+// FP8 32x32x64 and 12 after the 8-pass BF16 32x32x16, and 24 cover both.  Being
+// volatile and tied to every accumulator, this also keeps all of those MFMAs in uniform
+// control flow ahead of it.  (tests/test_mfma_hazards.py checks the built code.)
 __device__ __forceinline__ void vacc_settle(f32x16 (&o)[4], f32x16& l) {
     asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+v"(o[0]), "+v"(o[1]), "+v"(o[2]), "+v"(o[3]), "+v"(l));
 }

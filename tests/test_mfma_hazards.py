@@ -9,11 +9,19 @@ register copy or a rematerialised constant placed by the compiler just ahead of 
 an MFMA makes it read the old register contents: rows of the output then change with
 the register allocation of the kernel variant.
 
+Results: an XDL MFMA's destination registers may be read or written by a non-matrix
+instruction only after a number of wait states that grows with its passes.  The compiler
+inserts, for its own builtin MFMAs on gfx950 (compiling a builtin followed by a vector
+read shows it), 20 wait states after a 16-pass v_mfma(_scale)_f32_32x32x64_f8f6f4 and 12
+after an 8-pass v_mfma_f32_32x32x16_bf16; after the inline-asm ones, vacc_settle's three
+s_nop 7 give 24.
+
 This test disassembles the gfx950 code objects of libattnfwd.so (llvm-objdump) and
 checks, for every MFMA of every kernel, that no vector instruction within the two
-wait states before it writes one of its source registers (s_nop N counts N+1 wait
-states, any other instruction one).  The scan follows the code layout backwards and
-stops at a branch, so it sees fall-through predecessors only.
+wait states before it writes one of its source registers, and that no non-matrix
+instruction touches its destination registers within the wait states above (s_nop N
+counts N+1 wait states, any other instruction one).  The scans follow the code layout
+and stop at a branch, so they see fall-through neighbours only.
 """
 import os
 import re
@@ -87,6 +95,33 @@ def find_hazards(functions, need=VALU_TO_MFMA_WAIT_STATES):
     return checked, bad
 
 
+RESULT_WAIT_STATES = {"v_mfma_scale_f32_32x32x64_f8f6f4": 20, "v_mfma_f32_32x32x64_f8f6f4": 20,
+                      "v_mfma_f32_32x32x16_bf16": 12}
+
+
+def find_result_hazards(functions):
+    """(number of MFMAs checked, [(function, mfma, toucher, wait states between)])."""
+    checked, bad = 0, []
+    for name, ins in functions.items():
+        for i, (mn, ops) in enumerate(ins):
+            need = RESULT_WAIT_STATES.get(mn)
+            if need is None or not ops:
+                continue
+            checked += 1
+            dst = _vgprs(ops[0])
+            w, j = 0, i + 1
+            while j < len(ins) and w < need:
+                m2, o2 = ins[j]
+                if m2.startswith(("s_branch", "s_cbranch", "s_setpc", "s_endpgm")):
+                    break
+                if not m2.startswith(("v_mfma", "s_")) and set().union(set(), *(_vgprs(o) for o in o2)) & dst:
+                    bad.append((name, f"{mn} {', '.join(ops)}", f"{m2} {', '.join(o2)}", w))
+                    break
+                w += _wait_states(m2, o2)
+                j += 1
+    return checked, bad
+
+
 def test_checker_flags_a_planted_hazard():
     # the checker itself: a vector move into an A-operand register right ahead of the MFMA
     # is flagged; the same move two wait states earlier (s_nop 1) is not
@@ -104,6 +139,20 @@ def test_checker_flags_a_planted_hazard():
     assert checked == 3
     assert [b[3] for b in bad] == [0, 0]            # the first and the third (scale operand)
     assert "v[96:97]" in bad[0][1] and "v146" in bad[1][1]
+    # a result read 19 wait states after a 16-pass MFMA is flagged, 20 is not
+    dis2 = """
+0000000000002000 <k2>:
+	v_mfma_f32_32x32x64_f8f6f4 v[2:17], v[18:25], v[26:33], 0 // 000000002000: 00000000
+	s_nop 15                                                   // 000000002008: 00000000
+	s_nop 2                                                    // 00000000200c: 00000000
+	v_add_f32_e32 v1, v2, v7                                   // 000000002010: 00000000
+	v_mfma_f32_32x32x64_f8f6f4 v[2:17], v[18:25], v[26:33], 0 // 000000002014: 00000000
+	s_nop 15                                                   // 00000000201c: 00000000
+	s_nop 3                                                    // 000000002020: 00000000
+	v_add_f32_e32 v1, v2, v7                                   // 000000002024: 00000000
+"""
+    checked, bad = find_result_hazards(_functions(dis2))
+    assert checked == 2 and len(bad) == 1 and bad[0][3] == 19
 
 
 def test_no_vector_write_just_ahead_of_an_mfma(tmp_path):
@@ -121,4 +170,7 @@ def test_no_vector_write_just_ahead_of_an_mfma(tmp_path):
         functions.update(_functions(dis))
     checked, bad = find_hazards(functions)
     assert checked > 1000, checked                  # every attention kernel's MFMAs were seen
+    assert not bad, bad[:5]
+    checked, bad = find_result_hazards(functions)
+    assert checked > 1000, checked
     assert not bad, bad[:5]
