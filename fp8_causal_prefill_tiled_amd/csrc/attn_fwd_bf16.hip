@@ -491,16 +491,17 @@ __global__ void __launch_bounds__(512) bf16_causal_fwd(Bf16Params a) {
     const float lsumd = (VARLEN && !(lsum > 0.0f)) ? INFINITY : lsum;
     if (LSE && hh == 0 && qabs < S)
         a.lse[(VARLEN ? (int64_t)h * a.total + tok0 : ((int64_t)b * a.Hq + h) * S) + qabs] = (log2f(lsum) + ref) * 0.6931471805599453f;
+    const Quotient quot(lsumd);   // O / l, one reciprocal for the lane's 64 values
     if (qabs < S) {
         __bf16* op = a.o + ((tok0 + qabs) * a.Hq + h) * 128;
 #pragma unroll
         for (int dt = 0; dt < 4; ++dt) {
 #pragma unroll
             for (int r4 = 0; r4 < 4; ++r4) {
-                float x0 = o[dt][4 * r4 + 0] / lsumd;
-                float x1 = o[dt][4 * r4 + 1] / lsumd;
-                float x2 = o[dt][4 * r4 + 2] / lsumd;
-                float x3 = o[dt][4 * r4 + 3] / lsumd;
+                float x0 = quot(o[dt][4 * r4 + 0]);
+                float x1 = quot(o[dt][4 * r4 + 1]);
+                float x2 = quot(o[dt][4 * r4 + 2]);
+                float x3 = quot(o[dt][4 * r4 + 3]);
                 uint2 pk = make_uint2(pack_bf16x2(x0, x1), pack_bf16x2(x2, x3));
                 *reinterpret_cast<uint2*>(op + 32 * dt + 8 * r4 + 4 * hh) = pk;
             }

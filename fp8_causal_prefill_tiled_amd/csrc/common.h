@@ -165,6 +165,25 @@ __device__ __forceinline__ void block_sync() {
     __builtin_amdgcn_sched_barrier(0);
 }
 
+// x / b for many x and one b (the epilogues' O / L): one reciprocal refined by a Newton step,
+// then per value q = x y corrected by its residual x - b q (exact with an FMA), Markstein's
+// final division step, which rounds like the division itself for the normal b of the
+// epilogues (b within a few binades of 1).  b = infinity (a row without keys, x = 0) gives 0:
+// y = 0, and the residual uses b = 0 (infinity times the zero quotient would be NaN).
+struct Quotient {
+    float b, y;
+    __device__ __forceinline__ explicit Quotient(float b_) {
+        const bool inf = b_ == INFINITY;
+        const float r = __builtin_amdgcn_rcpf(b_);
+        y = inf ? 0.0f : fmaf(fmaf(-b_, r, 1.0f), r, r);
+        b = inf ? 0.0f : b_;
+    }
+    __device__ __forceinline__ float operator()(float x) const {
+        const float q = x * y;
+        return fmaf(fmaf(-b, q, x), y, q);
+    }
+};
+
 __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
     __bf16 x = (__bf16)a, y = (__bf16)b;
     return (uint32_t)__builtin_bit_cast(uint16_t, x) | ((uint32_t)__builtin_bit_cast(uint16_t, y) << 16);

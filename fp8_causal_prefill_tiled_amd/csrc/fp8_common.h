@@ -185,16 +185,17 @@ __device__ __forceinline__ void store_out(const Fp8Params& a, const Work& u, int
     if (LSE && hh == 0 && qabs < u.S)
         a.lse[(VARLEN ? (int64_t)u.h * a.total + u.tok0 : ((int64_t)u.b * a.Hq + u.h) * u.S) + qabs] =
             (log2f(l0) + ref) * 0.6931471805599453f;
+    const Quotient quot(l0d);   // O / L, one reciprocal for the lane's 64 values
     if (qabs < u.S) {
         __bf16* op = a.o + ((u.tok0 + qabs) * a.Hq + u.h) * 128;
 #pragma unroll
         for (int dt = 0; dt < 4; ++dt) {
 #pragma unroll
             for (int r4 = 0; r4 < 4; ++r4) {
-                float x0 = (o[dt][4 * r4 + 0] / l0d) * sc_v;
-                float x1 = (o[dt][4 * r4 + 1] / l0d) * sc_v;
-                float x2 = (o[dt][4 * r4 + 2] / l0d) * sc_v;
-                float x3 = (o[dt][4 * r4 + 3] / l0d) * sc_v;
+                float x0 = quot(o[dt][4 * r4 + 0]) * sc_v;
+                float x1 = quot(o[dt][4 * r4 + 1]) * sc_v;
+                float x2 = quot(o[dt][4 * r4 + 2]) * sc_v;
+                float x3 = quot(o[dt][4 * r4 + 3]) * sc_v;
                 uint2 pk = make_uint2(pack_bf16x2(x0, x1), pack_bf16x2(x2, x3));
                 *reinterpret_cast<uint2*>(op + 32 * dt + 8 * r4 + 4 * hh) = pk;
             }
